@@ -1,0 +1,390 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden/, each file citing its page and section), closed
+forms, special cases that reduce to a library routine, invariants, and brute
+force on tiny inputs.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from mixture_experts_ffn_08_amd import inputs
+
+
+# ---------------------------------------------------------------- router ----
+
+def test_worked_example_renormalized(golden):
+    g = golden("router_worked_example.txt")
+    probs = np.array(g["probs"], np.float64)
+    keys = np.log(probs).astype(np.float32)[None, :]        # softmax(ln p) = p
+    idx, near = oracle.top_k(keys, int(g["k"]))
+    assert list(idx[0] + 1) == [int(v) for v in g["chosen_1based"]]
+    w = oracle.gate_weights(keys, idx, oracle.SOFTMAX_THEN_TOPK, renorm=True)
+    np.testing.assert_allclose(w[0], g["weights_renorm"], rtol=1e-6)
+    # The Mixtral-style mode (softmax over the chosen scores) gives the same weights.
+    w2 = oracle.gate_weights(keys, idx, oracle.TOPK_THEN_SOFTMAX, renorm=False)
+    np.testing.assert_allclose(w2[0], g["weights_renorm"], rtol=1e-6)
+    # Without renormalization the raw probabilities remain (sum < 1).
+    w3 = oracle.gate_weights(keys, idx, oracle.SOFTMAX_THEN_TOPK, renorm=False)
+    np.testing.assert_allclose(w3[0], probs[:2], rtol=1e-6)
+    assert near[0] == 0
+
+
+def test_softmax_matches_scipy():
+    rng = np.random.default_rng(1)
+    s = rng.normal(size=(37, 19)) * 5
+    np.testing.assert_allclose(oracle.softmax(s), scipy.special.softmax(s, axis=-1), rtol=1e-13, atol=1e-300)
+
+
+def test_modes_agree_and_weight_sums():
+    rng = np.random.default_rng(2)
+    s = rng.normal(size=(200, 16)).astype(np.float32)
+    idx, _ = oracle.top_k(s, 4)
+    wa = oracle.gate_weights(s, idx, oracle.SOFTMAX_THEN_TOPK, renorm=True)
+    wb = oracle.gate_weights(s, idx, oracle.TOPK_THEN_SOFTMAX, renorm=False)
+    np.testing.assert_allclose(wa, wb, rtol=2e-7)
+    np.testing.assert_allclose(wa.sum(1), 1.0, rtol=1e-6)
+    wc = oracle.gate_weights(s, idx, oracle.SOFTMAX_THEN_TOPK, renorm=False)
+    assert np.all(wc.sum(1) < 1.0)
+    # raw weights are the full-softmax probabilities of the chosen experts
+    p = scipy.special.softmax(s.astype(np.float64), axis=-1)
+    np.testing.assert_allclose(wc, np.take_along_axis(p, idx.astype(np.int64), 1), rtol=1e-6)
+    # slots come in descending weight order
+    assert np.all(np.diff(wc, axis=1) <= 0)
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (6, 3), (8, 2), (9, 4), (7, 7)])
+def test_topk_brute_force_over_subsets(E, k):
+    """The chosen set is the max-sum subset; among equal sums the lexicographically
+    smallest index set (the lower-index rule).  Integer keys force many ties."""
+    rng = np.random.default_rng(E * 31 + k)
+    keys = rng.integers(-3, 4, size=(300, E)).astype(np.float32)
+    idx, _ = oracle.top_k(keys, k)
+    for t in range(keys.shape[0]):
+        best = max(itertools.combinations(range(E), k),
+                   key=lambda c: (sum(keys[t, list(c)]), [-i for i in c]))
+        assert sorted(idx[t].tolist()) == list(best)
+        # slot order: descending score, lower index first on equal scores
+        order = sorted(best, key=lambda e: (-keys[t, e], e))
+        assert idx[t].tolist() == order
+
+
+def test_topk_all_equal_scores_take_lowest_indices():
+    keys = np.zeros((5, 8), np.float32)
+    idx, near = oracle.top_k(keys, 3)
+    assert (idx == np.array([0, 1, 2])).all()
+    assert (near == 1).all()
+
+
+def test_near_tie_flag():
+    keys = np.array([[1.0, 0.5, 0.5 - 5e-5, 0.0], [1.0, 0.5, 0.4, 0.0]], np.float32)
+    _, near = oracle.top_k(keys, 2)
+    assert near.tolist() == [1, 0]
+    _, near_full = oracle.top_k(keys, 4)
+    assert near_full.tolist() == [0, 0]
+
+
+def test_active_set_counts(golden):
+    g = golden("active_sets.txt")
+    assert sum(1 for _ in itertools.combinations(range(16), 2)) == g["c_16_2"]
+    assert sum(1 for _ in itertools.combinations(range(8), 2)) == g["c_8_2"]
+    assert sum(1 for _ in itertools.combinations(range(4), 2)) == g["c_4_2"]
+    assert math.comb(32, 8) > g["c_32_8_at_least"]
+    ex = golden("exercises_tm17.txt")
+    assert round(math.comb(64, 8) / 1e9, 2) == ex["choose_64_8_billions"]
+
+
+# -------------------------------------------------------------- capacity ----
+
+def test_capacity_exercise(golden):
+    g = golden("exercises_tm17.txt")
+    assert oracle.capacity(int(g["capacity_tokens"]), int(g["capacity_k"]),
+                           int(g["capacity_experts"]), g["capacity_gamma"]) == g["capacity_expected"]
+
+
+def test_capacity_closed_forms():
+    assert oracle.capacity(4096, 2, 8, 1.25) == 1280          # Mixtral-shaped layer, phi = 1.25
+    assert oracle.capacity(64, 2, 8, 1.0) == 16                # exact integer: no bump
+    assert oracle.capacity(63, 2, 8, 1.0) == 16                # 15.75 rounds up
+    assert oracle.capacity(64, 2, 8, 0.5) == 8                 # phi below one is allowed
+    assert oracle.capacity(10, 1, 1, 0.3) == 3                 # double(0.3) < 0.3: ceil(2.99..) = 3
+    assert oracle.capacity(5, 3, 7, None) is None
+    for T, k, E, phi in [(1000, 3, 7, 1.1), (999, 2, 5, 1.7), (4096, 8, 64, 2.0)]:
+        c = oracle.capacity(T, k, E, phi)
+        assert c - 1 < phi * T * k / E <= c + 1e-9
+
+
+def _rank_by_definition(idx):
+    """rank[t][j] = number of earlier tokens t' < t that also chose idx[t][j]."""
+    T, k = idx.shape
+    rank = np.zeros((T, k), np.int64)
+    for t in range(T):
+        for j in range(k):
+            rank[t, j] = sum(1 for u in range(t) if idx[t, j] in idx[u])
+    return rank
+
+
+def _random_routing(rng, T, E, k, skew=0.0):
+    scores = rng.normal(size=(T, E)) + skew * np.linspace(1, 0, E)[None, :]
+    return oracle.top_k(scores.astype(np.float32), k)[0]
+
+
+@pytest.mark.parametrize("T,E,k,phi", [(40, 4, 1, 0.5), (37, 6, 2, 1.0), (50, 8, 3, 1.25), (23, 5, 5, 0.7)])
+def test_dispatch_brute_force(T, E, k, phi):
+    rng = np.random.default_rng(T + E + k)
+    idx = _random_routing(rng, T, E, k, skew=1.5)
+    cap = oracle.capacity(T, k, E, phi)
+    counts, offsets, row_of, perm_token = oracle.dispatch(idx, E, cap)
+    rank = _rank_by_definition(idx)
+    for e in range(E):
+        assert counts[e] == int((idx == e).sum())
+        assert offsets[e + 1] - offsets[e] == min(counts[e], cap)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if rank[t, j] < cap:
+                assert row_of[t, j] == offsets[e] + rank[t, j]
+                assert perm_token[row_of[t, j]] == t
+            else:
+                assert row_of[t, j] == -1
+
+
+def test_dispatch_invariants():
+    rng = np.random.default_rng(5)
+    T, E, k = 300, 16, 4
+    idx = _random_routing(rng, T, E, k, skew=3.0)
+    for cap in (None, oracle.capacity(T, k, E, 1.0), 1, 0):
+        counts, offsets, row_of, perm_token = oracle.dispatch(idx, E, cap)
+        assert counts.sum() == T * k
+        kept = np.diff(offsets)
+        assert np.all(kept >= 0) and offsets[0] == 0
+        if cap is not None:
+            assert np.all(kept <= cap)
+        rows = row_of[row_of >= 0]
+        assert sorted(rows.tolist()) == list(range(offsets[-1]))    # bijection onto [0, R)
+        for e in range(E):
+            toks = perm_token[offsets[e]:offsets[e + 1]]
+            assert np.all(np.diff(toks) > 0)                        # ascending tokens, each once
+
+
+# --------------------------------------------------------------- experts ----
+
+def test_silu_matches_torch():
+    z = np.linspace(-40, 40, 2001)
+    np.testing.assert_allclose(oracle.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-14, atol=1e-300)
+
+
+def _tiny_layer(rng, T, d, E, k, F, Fs):
+    x = rng.normal(size=(T, d)).astype(np.float32)
+    wr = (rng.normal(size=(E, d)) / np.sqrt(d)).astype(np.float32)
+    ex = [((rng.normal(size=(F, d)) / np.sqrt(d)).astype(np.float32),
+           (rng.normal(size=(F, d)) / np.sqrt(d)).astype(np.float32),
+           (rng.normal(size=(d, F)) / np.sqrt(F)).astype(np.float32)) for _ in range(E)]
+    sh = None if Fs == 0 else ((rng.normal(size=(Fs, d)) / np.sqrt(d)).astype(np.float32),
+                              (rng.normal(size=(Fs, d)) / np.sqrt(d)).astype(np.float32),
+                              (rng.normal(size=(d, Fs)) / np.sqrt(Fs)).astype(np.float32))
+    return x, wr, ex, sh
+
+
+def _torch_swiglu(x, g, u, dn):
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    G, U, D = (torch.from_numpy(np.asarray(m, np.float64)) for m in (g, u, dn))
+    return (torch.nn.functional.silu(X @ G.T) * (X @ U.T) @ D.T).numpy()
+
+
+def test_one_expert_moe_is_the_dense_mlp():
+    """With E = 1 and k = 1 the layer is the dense SwiGLU MLP (The Residual Stream,
+    "A bug worth knowing about": a one-expert MoE equals the dense MLP)."""
+    rng = np.random.default_rng(7)
+    x, wr, ex, _ = _tiny_layer(rng, 33, 16, 1, 1, 24, 0)
+    out = oracle.layer_forward(x, wr, None, lambda e: ex[e], None, k=1, mode=oracle.SOFTMAX_THEN_TOPK,
+                               renorm=False, phi=None, alpha=0.01, dtype="f32")
+    np.testing.assert_allclose(out["w"], 1.0)
+    np.testing.assert_allclose(out["y64"], _torch_swiglu(x, *ex[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_identical_experts_renormalized_equal_one_expert_plus_shared():
+    rng = np.random.default_rng(8)
+    x, wr, ex, sh = _tiny_layer(rng, 29, 16, 6, 3, 20, 12)
+    out = oracle.layer_forward(x, wr, None, lambda e: ex[0], sh, k=3, mode=oracle.SOFTMAX_THEN_TOPK,
+                               renorm=True, phi=None, alpha=0.01, dtype="f32")
+    ref = _torch_swiglu(x, *ex[0]) + _torch_swiglu(x, *sh)
+    np.testing.assert_allclose(out["y64"], ref, rtol=1e-6, atol=1e-9)
+
+
+@pytest.mark.parametrize("mode,renorm,phi,Fs", [(oracle.TOPK_THEN_SOFTMAX, False, None, 0),
+                                                (oracle.SOFTMAX_THEN_TOPK, False, None, 10),
+                                                (oracle.SOFTMAX_THEN_TOPK, True, 0.75, 0),
+                                                (oracle.TOPK_THEN_SOFTMAX, False, 1.0, 10)])
+def test_layer_equals_per_token_sum_with_torch_experts(mode, renorm, phi, Fs):
+    """Permute / grouped experts / combine equals the per-token sum of the
+    definition, each expert evaluated by torch (library silu and matmul)."""
+    rng = np.random.default_rng(11)
+    T, d, E, k, F = 45, 16, 6, 2, 24
+    x, wr, ex, sh = _tiny_layer(rng, T, d, E, k, F, Fs)
+    out = oracle.layer_forward(x, wr, None, lambda e: ex[e], sh, k=k, mode=mode, renorm=renorm,
+                               phi=phi, alpha=0.01, dtype="f32")
+    per_expert = [_torch_swiglu(x, *ex[e]) for e in range(E)]
+    shared = 0 if sh is None else _torch_swiglu(x, *sh)
+    ref = np.zeros((T, d)) + shared
+    for t in range(T):
+        for j in range(k):
+            if out["row_of"][t, j] >= 0:
+                ref[t] += float(out["w"][t, j]) * per_expert[out["idx"][t, j]][t]
+    np.testing.assert_allclose(out["y64"], ref, rtol=1e-6, atol=1e-9)
+    if phi is not None:
+        assert (out["row_of"] < 0).any(), "case meant to drop assignments"
+    # token_output follows the same definition
+    kept = out["row_of"] >= 0
+    for t in (0, T // 2, T - 1):
+        yt = oracle.token_output(x[t], out["idx"][t], out["w"][t], kept[t], lambda e: ex[e], sh)
+        np.testing.assert_allclose(yt, ref[t], rtol=1e-6, atol=1e-9)
+
+
+def test_dropped_slot_keeps_other_weights_unrenormalized():
+    """A token dropped by one expert keeps its other expert at the original weight
+    (Transformers & Math 17.5; ML Interview Notes "Capacity factor")."""
+    x = np.zeros((3, 4), np.float32)
+    x[:, 0] = 1.0
+    wr = np.zeros((2, 4), np.float32)
+    wr[0, 0], wr[1, 0] = 2.0, 1.0                              # every token prefers expert 0, then 1
+    g = np.eye(4, dtype=np.float32)
+    ex = [(g, g, g), (2 * g, g, g)]
+    out = oracle.layer_forward(x, wr, None, lambda e: ex[e], None, k=2, mode=oracle.TOPK_THEN_SOFTMAX,
+                               renorm=False, phi=0.5, alpha=0.01, dtype="f32")
+    assert out["capacity"] == 2
+    assert out["row_of"][2].tolist() == [-1, -1]
+    assert out["row_of"][0].min() >= 0 and out["row_of"][1].min() >= 0
+    np.testing.assert_array_equal(out["y64"][2], 0.0)
+    w = out["w"][0]
+    np.testing.assert_allclose(w, scipy.special.softmax([2.0, 1.0]), rtol=1e-6)
+
+
+# ----------------------------------------------------------------- stats ----
+
+def _even_top1_scores(T, E, L):
+    s = np.zeros((T, E), np.float32)
+    s[np.arange(T), np.arange(T) % E] = L
+    return s
+
+
+def test_laux_even_top1_is_alpha(golden):
+    g = golden("exercises_tm17.txt")
+    E, alpha = int(g["laux_experts"]), g["laux_alpha"]
+    s = _even_top1_scores(8 * E, E, 3.0)
+    idx, _ = oracle.top_k(s, 1)
+    counts, *_ = oracle.dispatch(idx, E, None)
+    f, P, l_aux, mom = oracle.balance_stats(counts, s, s.shape[0], 1, E, alpha)
+    np.testing.assert_allclose(f, 1.0 / E)
+    np.testing.assert_allclose(P, 1.0 / E, rtol=1e-6)
+    assert l_aux == pytest.approx(g["laux_even_expected"], rel=1e-6)
+    assert mom == 1.0
+
+
+def test_laux_collapsed_is_alpha_times_experts(golden):
+    g = golden("exercises_tm17.txt")
+    E, alpha = int(g["laux_experts"]), g["laux_alpha"]
+    s = np.zeros((64, E), np.float32)
+    s[:, 0] = 1000.0                                           # probability 1 on expert 1
+    idx, _ = oracle.top_k(s, 1)
+    counts, *_ = oracle.dispatch(idx, E, None)
+    f, P, l_aux, _ = oracle.balance_stats(counts, s, 64, 1, E, alpha)
+    assert f[0] == 1.0 and P[0] == 1.0
+    assert l_aux == pytest.approx(g["laux_collapsed_expected"], rel=1e-6)
+
+
+def test_lbal_uniform_and_collapsed(golden):
+    g = golden("balance_loss_rs.txt")
+    for E in (4, 8, 16):
+        s = _even_top1_scores(4 * E, E, 2.0)
+        idx, _ = oracle.top_k(s, 1)
+        counts, *_ = oracle.dispatch(idx, E, None)
+        _, _, l, _ = oracle.balance_stats(counts, s, 4 * E, 1, E, alpha=1.0)
+        assert l == pytest.approx(g["lbal_uniform"], rel=1e-6)
+        s2 = np.zeros((4 * E, E), np.float32)
+        s2[:, E - 1] = 1000.0
+        idx2, _ = oracle.top_k(s2, 1)
+        counts2, *_ = oracle.dispatch(idx2, E, None)
+        _, _, l2, _ = oracle.balance_stats(counts2, s2, 4 * E, 1, E, alpha=1.0)
+        assert l2 == pytest.approx(E * g["lbal_collapsed_is_E"], rel=1e-6)
+
+
+def test_worst_case_imbalance_collapsed_top2(golden):
+    g = golden("load_imbalance_ud.txt")
+    E, k = int(g["E"]), int(g["k"])
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(256, 32)).astype(np.float32)
+    wr = (rng.normal(size=(E, 32)) / np.sqrt(32)).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[[3, 5]] = 100.0                                        # collapsed router
+    s, idx, _, _ = oracle.route(x, wr, bias, k, oracle.SOFTMAX_THEN_TOPK, True)
+    counts, *_ = oracle.dispatch(idx, E, None)
+    _, _, _, mom = oracle.balance_stats(counts, s, 256, k, E, 0.01)
+    assert mom == g["worst_case_max_over_mean"]
+    # a zero router ties every expert: the lower indices win and the load collapses too
+    s0, idx0, _, near0 = oracle.route(x, np.zeros_like(wr), None, k, oracle.SOFTMAX_THEN_TOPK, True)
+    assert (idx0 == np.arange(k)).all() and (near0 == 1).all()
+    counts0, *_ = oracle.dispatch(idx0, E, None)
+    assert oracle.balance_stats(counts0, s0, 256, k, E, 0.01)[3] == E / k
+    # random routing stays inside [1, E/k]
+    s1, idx1, _, _ = oracle.route(x, wr, None, k, oracle.SOFTMAX_THEN_TOPK, True)
+    counts1, *_ = oracle.dispatch(idx1, E, None)
+    assert 1.0 <= oracle.balance_stats(counts1, s1, 256, k, E, 0.01)[3] <= E / k
+
+
+def test_f_is_bit_exact_float32_division():
+    counts = np.array([3, 0, 7, 1, 1, 0, 2, 2], np.int32)
+    f, *_ = oracle.balance_stats(counts, np.zeros((8, 8), np.float32), 8, 2, 8, 0.01)
+    for c, fi in zip(counts, f):
+        assert fi == np.float32(float(c) / 16.0)               # exact in binary
+
+
+# ---------------------------------------------------------- sizes/counts ----
+
+def test_expert_sizes_match_pages(golden):
+    g = golden("counting_rs.txt")
+    mx, ds = inputs.SHAPES["mixtral"], inputs.SHAPES["dsv3_skew"]
+    per = 3 * mx.d * mx.F
+    assert round(per / 1e6) == g["mixtral_expert_millions"]
+    assert round(per * mx.E * 32 / 1e9, 1) == g["mixtral_all_layers_billions"]
+    assert round(per * mx.k * 32 / 1e9, 1) == g["mixtral_used_per_token_billions"]
+    assert round(3 * ds.d * ds.F / 1e6) == g["dsv3_routed_expert_millions"]
+
+
+def test_experts_touched_closed_form(golden):
+    g = golden("counting_rs.txt")
+    E, k = int(g["touched_E"]), int(g["touched_k"])
+    for B, want, per in zip(g["touched_B"], g["touched_experts"], g["touched_tokens_per_expert"]):
+        got = oracle.experts_touched_expected(E, k, int(B))
+        assert round(got, 1) == want
+        assert round(B * k / got, 1) == per
+
+
+def test_experts_touched_closed_form_monte_carlo():
+    rng = np.random.default_rng(0)
+    E, k, B = 64, 4, 16
+    touched = [len({e for _ in range(B) for e in rng.choice(E, k, replace=False)}) for _ in range(4000)]
+    assert np.mean(touched) == pytest.approx(oracle.experts_touched_expected(E, k, B), rel=0.01)
+
+
+# -------------------------------------------------------------- rounding ----
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(9)
+    v = np.concatenate([rng.normal(size=5000), rng.normal(size=5000) * 1e-3, [0.0, -0.0, 1.0, -2.5]])
+    v32 = v.astype(np.float32).astype(np.float64)               # float32-exact inputs
+    ours = oracle.round_to_bf16(v32)
+    ref = torch.from_numpy(v32.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    # halfway cases round to even
+    assert oracle.round_to_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert oracle.round_to_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    # the generator's rounding agrees with torch's as well
+    np.testing.assert_array_equal(inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(v32.astype(np.float32))), ref)
