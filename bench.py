@@ -1,0 +1,193 @@
+"""Benchmark: one forward pass of the Qwen3-30B-A3B-shaped MoE layer per step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload qwen3_prefill]
+
+A step is the whole layer (route, permute, grouped gate/up, grouped down,
+shared expert when present, combine, stats) on T tokens already resident in
+HBM, enqueued on one stream through the C ABI of libmoe.so.  K steps are timed
+with HIP events between two device synchronizations.  Prints one JSON line:
+tokens/s, the roofline of the dominant kernel (the grouped gate/up GEMM, timed
+with events on its own stream around each launch), the grouped-GEMM share of
+the bf16 MFMA peak, the decode-regime layer against HBM bandwidth, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 256 * 4096 * 2.4e9      # dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM_BYTES = 8.0e12                   # HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen3_prefill")
+    p.add_argument("--decode-workload", default="qwen3_decode")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    return p.parse_args()
+
+
+def timed_steps(layer, x, bufs, steps, warmup, stream, torch):
+    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down)."""
+    from mixture_experts_ffn_08_amd import _lib
+
+    s = layer.shape
+    R = bufs.T * s.k
+
+    def step(ev=None):
+        layer.route(x, bufs, stream)
+        layer.permute(x, bufs, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        _lib.moe_grouped_gate_up(bufs.x_perm, bufs.offsets, s.E, R, s.d, s.F, layer.w.gate, layer.w.up, bufs.a,
+                                 stream)
+        if ev is not None:
+            ev[1].record(stream)
+        _lib.moe_grouped_down(bufs.a, bufs.offsets, s.E, R, s.F, s.d, layer.w.down, bufs.y_perm, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        layer.shared_expert(x, bufs, stream)
+        layer.combine(bufs, stream)
+        layer.stats(bufs, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    gu = [e[0].elapsed_time(e[1]) for e in evs]
+    dn = [e[1].elapsed_time(e[2]) for e in evs]
+    return total / steps, float(np.mean(gu)), float(np.mean(dn))
+
+
+def cpu_baseline(inp, target_s):
+    """The oracle, as it stands, on a growing prefix of the workload's tokens until
+    it has run for about target_s seconds; tokens/s of the last sample."""
+    import oracle
+    from mixture_experts_ffn_08_amd import inputs as minp
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    s = inp.shape
+    ex = {}
+
+    def weights(e):
+        if e not in ex:
+            ex[e] = tuple(minp.as_f32(m, s.dtype) for m in inp.expert(e))
+        return ex[e]
+
+    for e in range(s.E):
+        weights(e)
+    sh = inp.shared()
+    sh = None if sh is None else tuple(minp.as_f32(m, s.dtype) for m in sh)
+    xs = minp.as_f32(inp.x, s.dtype)
+    wr = minp.as_f32(inp.w_router, s.dtype)
+    n, elapsed = 64, 0.0
+    while True:
+        n = min(n, s.T)
+        t0 = time.perf_counter()
+        oracle.layer_forward(xs[:n], wr, inp.bias, weights, sh, k=s.k, mode=s.mode, renorm=s.renorm, phi=s.phi,
+                             alpha=s.alpha, dtype=s.dtype)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s or n == s.T:
+            break
+        n = int(n * min(8.0, max(1.5, 1.1 * target_s / max(elapsed, 1e-3))))
+    return {"value": n / elapsed, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens of the {s.name} layer, full oracle forward (float64), "
+                      f"{elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
+              f"(there is no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_ffn_08_amd import inputs as minp
+    from mixture_experts_ffn_08_amd.layer import Buffers, DeviceWeights, MoeLayer, to_device
+
+    torch.cuda.set_device(0)
+    shape = minp.SHAPES[args.workload]
+    inp = minp.LayerInputs(shape, seed=0)
+    weights = DeviceWeights(inp, "cuda:0")
+    layer = MoeLayer(weights)
+    x = to_device(inp.x, shape.dtype, "cuda:0")
+    bufs = Buffers(shape, shape.T, "cuda:0")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, args.steps, args.warmup, stream, torch)
+    R = int(bufs.offsets[-1].item())
+    flops_gu = 4.0 * R * shape.d * shape.F
+    flops_dn = 2.0 * R * shape.F * shape.d
+    achieved = flops_gu / (gu_ms * 1e-3)
+    result = {
+        "metric": "MoE-layer tokens/s (Qwen3-30B-A3B shape, bf16); grouped-GEMM % of MFMA peak",
+        "value": shape.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: T={shape.T} d={shape.d} E={shape.E} top-{shape.k} "
+                               f"SwiGLU F={shape.F}, softmax over all then renormalized, dropless, seed 0",
+                   "global_batch": shape.T, "parallelism": "single GPU"},
+        "roofline": {"kernel": "grouped gate/up GEMM (+SiLU*up)", "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS,
+                     "traffic": None, "launch_ms": gu_ms},
+        "grouped_gemm": {"ms": gu_ms + dn_ms, "tflops": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / 1e12,
+                         "frac_of_mfma_peak": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / PEAK_BF16_FLOPS,
+                         "down_ms": dn_ms},
+    }
+    # decode regime on the same weights
+    if args.decode_workload:
+        dshape = minp.SHAPES[args.decode_workload]
+        assert (dshape.d, dshape.E, dshape.F, dshape.k) == (shape.d, shape.E, shape.F, shape.k)
+        dinp = minp.LayerInputs(dshape, seed=0)
+        dlayer = MoeLayer(weights)
+        dlayer.shape = dshape
+        dx = to_device(dinp.x, dshape.dtype, "cuda:0")
+        dbufs = Buffers(dshape, dshape.T, "cuda:0")
+        with torch.cuda.stream(stream):
+            dms, _, _ = timed_steps(dlayer, dx, dbufs, max(args.steps, 50), args.warmup, stream, torch)
+        touched = int((dbufs.counts > 0).sum().item())
+        dbytes = (touched * 3 * dshape.d * dshape.F + dshape.E * dshape.d + 2 * dshape.T * dshape.d) * 2
+        result["decode"] = {"workload": f"{dshape.name}: T={dshape.T}", "tokens_per_s": dshape.T / (dms * 1e-3),
+                            "ms_per_step": dms, "experts_touched": touched, "algorithmic_bytes": dbytes,
+                            "hbm_frac": dbytes / (dms * 1e-3) / PEAK_HBM_BYTES}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of one mixture-of-experts
+ * feed-forward layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages define it: a router scores every expert per token,
+ * keeps the k best and weights them (softmax over all experts then top-k,
+ * optionally renormalized, or top-k then softmax over the chosen k); tokens
+ * are grouped by expert, optionally capped at a capacity C; each expert is a
+ * SwiGLU MLP; an optional shared expert runs on every token; the outputs are
+ * summed back in token order, weighted by the gate weights; balance
+ * statistics f_i, P_i, L_aux and the demand max/mean load are reported.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory (HBM) of
+ *     the current device; the caller owns and allocates every buffer.  The
+ *     library keeps no state and allocates nothing.
+ *   - Tensors are dense, row-major.  Rows of x and of the weights must start on
+ *     16-byte boundaries (true when the base is 16-byte aligned and d, F are
+ *     multiples of 8).
+ *   - dtype (MOE_F32 or MOE_BF16) is the storage type of x, every weight
+ *     matrix, the hidden activations a, y_perm, shared_y and y.  Router scores
+ *     (logits), gate weights and statistics are float32.  Accumulation is
+ *     float32.  bfloat16 results are rounded to nearest, ties to even.
+ *   - Weights are held (out_features, in_features), as torch.nn.Linear holds
+ *     them: W_r[E][d]; per expert gate[F][d], up[F][d], down[d][F].
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *     synchronize the host.  Arguments are checked on the host before
+ *     anything is enqueued; on a bad argument a negative moe_status is
+ *     returned and nothing runs.  A failed launch returns MOE_ERR_HIP.
+ *     moe_last_error() describes the last failure on the calling thread.
+ *   - T = 0 (no tokens) is a valid call that enqueues nothing.
+ *   - Kernels never trap.  Values read from device memory that the host cannot
+ *     check (expert ids, offsets) are clamped or skipped as stated per call.
+ *
+ * Limits: 1 <= k <= E <= 256.  d and F multiples of 8 (MOE_F32) or of 128
+ * (MOE_BF16); other sizes return MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* NULL pointer, negative size, k > E, unknown enum, ... */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside the sizes the kernels handle */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than the *_workspace_bytes value */
+  MOE_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+enum moe_score_mode {
+  MOE_SOFTMAX_THEN_TOPK = 0, /* p = softmax over all E scores; weights = p of the chosen k */
+  MOE_TOPK_THEN_SOFTMAX = 1  /* weights = softmax over the chosen k scores */
+};
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_NEAR_TIE_GAP 1e-4
+
+/*
+ * moe_route -- router GEMM, top-k selection and gate weights.
+ * Sources: Latent "Mixture of experts", "Where the experts live" (s = W_r x and
+ * the gate equation); The Residual Stream "Mixture of Experts: More Parameters,
+ * Same FLOPs", "The router" (renormalized top-k equation, worked example);
+ * Transformers & Math 17.2 (the two softmax orders); ML Interview Notes, the
+ * Router listing.
+ *
+ *   x          device [T][d] dtype        token vectors
+ *   w_router   device [E][d] dtype        router weight (nn.Linear(d, E) layout)
+ *   logit_bias device [E] float32 or NULL added to every token's scores before
+ *                                        selection and softmax
+ *   logits     device [T][E] float32 out  s = x W_r^T (+ bias), float32 accumulation
+ *   topk_idx   device [T][k] int32 out    the k highest scores, best first; equal
+ *                                        scores go to the lower expert index
+ *   topk_w     device [T][k] float32 out  gate weights by `mode`; with
+ *                                        MOE_SOFTMAX_THEN_TOPK and renorm != 0 they
+ *                                        are divided by their sum (renorm is
+ *                                        ignored for MOE_TOPK_THEN_SOFTMAX)
+ *   near_tie   device [T] int32 out       1 where the k-th best score exceeds the
+ *                                        (k+1)-th by less than MOE_NEAR_TIE_GAP
+ *                                        (0 when k = E)
+ */
+int moe_route(const void* x, const void* w_router, const float* logit_bias, int dtype,
+              int T, int d, int E, int k, int mode, int renorm,
+              float* logits, int32_t* topk_idx, float* topk_w, int32_t* near_tie,
+              hipStream_t stream);
+
+/*
+ * moe_permute -- per-expert histogram, capacity, stable permutation, gather.
+ * Sources: ML Interview Notes, MoELayer listing (per-expert (token, slot) pairs)
+ * and "Capacity factor" (tokens arriving at a full expert are dropped);
+ * Transformers & Math 17.5 (capacity, dropped tokens keep their other experts);
+ * Understanding Data, "The maths", "Capacity".
+ *
+ * Assignment (t, j) goes to expert e = topk_idx[t][j].  Assignments reach their
+ * experts in ascending order of t*k + j; rank(t, j) is the number of earlier
+ * assignments to the same expert.  With capacity >= 0 an assignment is kept
+ * iff rank < capacity; capacity < 0 means dropless.  Expert ids outside [0, E)
+ * are ignored (counted nowhere, row -1).
+ *
+ *   counts     device [E] int32 out       demand per expert, before the cap
+ *   offsets    device [E+1] int32 out     offsets[0] = 0, offsets[e+1] =
+ *                                        offsets[e] + min(counts[e], capacity)
+ *   row_of     device [T][k] int32 out    offsets[e] + rank, or -1 when dropped
+ *   perm_token device [T*k] int32 out     token of each row; rows >= offsets[E]
+ *                                        are left untouched
+ *   x_perm     device [T*k][d] dtype out  x_perm[r] = x[perm_token[r]] for
+ *                                        r < offsets[E]
+ *   workspace  device, >= moe_permute_workspace_bytes(T, k, E) bytes, scratch
+ */
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity,
+                const void* x, int dtype, int d,
+                int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token,
+                void* x_perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t moe_permute_workspace_bytes(int T, int k, int E);
+
+/*
+ * moe_capacity -- C = ceil(phi * k * T / E), evaluated exactly on the binary
+ * value of phi (Transformers & Math 17.5 equation; Understanding Data,
+ * "Capacity").  Returns -1 (dropless) when phi is not finite or negative, or
+ * when T < 0, k < 1 or E < 1.
+ */
+int64_t moe_capacity(int64_t T, int k, int E, double phi);
+
+/*
+ * moe_grouped_gate_up -- first half of G SwiGLU experts as one variable-size
+ * grouped GEMM: for each group g and each row r in [offsets[g], offsets[g+1]),
+ *     a[r] = SiLU(x_perm[r] gate[g]^T) * (x_perm[r] up[g]^T),  SiLU(z) = z/(1+e^-z)
+ * Sources: The Residual Stream, "An MoE tiny GPT" listing (F.silu(h @ gate) *
+ * (h @ up)); ML Interview Notes "Capacity factor" (dropless routing with
+ * variable-size grouped GEMMs).
+ *
+ *   x_perm   device [max_rows][d] dtype
+ *   offsets  device [G+1] int32           group row ranges; values are clamped to
+ *                                        [0, max_rows]; rows outside every range
+ *                                        are not written
+ *   w_gate, w_up device [G][F][d] dtype
+ *   a        device [max_rows][F] dtype out
+ * G in [1, 256].  max_rows >= 0 bounds the launch; the true row count is read
+ * from offsets on the device, so no host round trip is needed.
+ */
+int moe_grouped_gate_up(const void* x_perm, const int32_t* offsets, int G, int max_rows,
+                        int d, int F, const void* w_gate, const void* w_up, int dtype,
+                        void* a, hipStream_t stream);
+
+/*
+ * moe_grouped_down -- second half: y_perm[r] = a[r] down[g]^T for r in group g.
+ *   a        device [max_rows][F] dtype
+ *   w_down   device [G][d][F] dtype
+ *   y_perm   device [max_rows][d] dtype out
+ */
+int moe_grouped_down(const void* a, const int32_t* offsets, int G, int max_rows,
+                     int F, int d, const void* w_down, int dtype, void* y_perm,
+                     hipStream_t stream);
+
+/*
+ * moe_grouped_swiglu -- moe_grouped_gate_up then moe_grouped_down: G SwiGLU
+ * experts (SiLU(h gate^T) * (h up^T)) down^T over their row groups.  The shared
+ * expert of a layer is this call with G = 1, offsets = {0, T} and x as x_perm
+ * (Transformers & Math 17.3; ML Interview Notes, MoELayer, always-on experts).
+ */
+int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int G, int max_rows,
+                       int d, int F, const void* w_gate, const void* w_up,
+                       const void* w_down, int dtype, void* a, void* y_perm,
+                       hipStream_t stream);
+
+/*
+ * moe_combine -- y[t] = sum over j with row_of[t][j] >= 0 of
+ *                topk_w[t][j] * y_perm[row_of[t][j]]  (+ shared_y[t]).
+ * Sources: Transformers & Math 17.2 equation (routed sum plus the shared
+ * expert, unweighted); ML Interview Notes, MoELayer (out[tok] += weights *
+ * expert(x)); Transformers & Math 17.5 (a dropped slot adds nothing and the
+ * other weights are kept as they are).
+ * The sum runs in slot order in float32 and is rounded once: the result is
+ * deterministic.  row_of values outside [0, T*k) count as dropped.
+ *
+ *   y_perm   device [T*k][d] dtype; row_of device [T][k] int32;
+ *   topk_w   device [T][k] float32; shared_y device [T][d] dtype or NULL;
+ *   y        device [T][d] dtype out (every row written)
+ */
+int moe_combine(const void* y_perm, const int32_t* row_of, const float* topk_w,
+                const void* shared_y, int dtype, int T, int k, int d, void* y,
+                hipStream_t stream);
+
+/*
+ * moe_stats -- balance statistics.
+ * Sources: Transformers & Math 17.4 equation (L_aux = alpha N_E sum f_i P_i);
+ * The Residual Stream "Keeping the load even" and the MoE listing (f = counts /
+ * counts.sum(), P = mean router probability); Latent "Keeping the load
+ * balanced"; Understanding Data "Load imbalance" (measured on demand).
+ *
+ *   counts   device [E] int32            demand per expert (moe_permute output)
+ *   logits   device [T][E] float32       router scores (moe_route output)
+ *   f        device [E] float32 out      counts[i] / (T k), one float32 division
+ *   P        device [E] float32 out      mean over tokens of softmax(logits[t])[i]
+ *   l_aux    device [1] float32 out      alpha * E * sum_i f_i P_i
+ *   max_over_mean device [1] float32 out E * max_i counts[i] / (T k)
+ *   workspace device, >= moe_stats_workspace_bytes(T, E) bytes, scratch
+ * With T = 0 nothing is written.
+ */
+int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, float alpha,
+              float* f, float* P, float* l_aux, float* max_over_mean,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t moe_stats_workspace_bytes(int T, int E);
+
+/* Human-readable name of a moe_status value. */
+const char* moe_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,200 @@
+"""ctypes binding of libmoe.so, one Python function per C entry point, same names.
+
+Argument marshalling only: tensors are checked (device, dtype, contiguity,
+size) so that no host pointer or short buffer reaches a kernel, then their
+device addresses are passed to the C function.  Every step of the layer runs in
+the library's HIP kernels; there is no fallback.  A non-zero status raises
+MoeError carrying moe_last_error().
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX_THEN_TOPK, MOE_TOPK_THEN_SOFTMAX = 0, 1
+MOE_MAX_EXPERTS = 256
+
+EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_capacity",
+           "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
+           "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_permute": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_capacity": (_I64, [_I64, _I, _I, ctypes.c_double]),
+    "moe_grouped_gate_up": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "moe_grouped_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
+    "moe_grouped_swiglu": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P]),
+    "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_stats": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_stats_workspace_bytes": (_SZ, [_I, _I]),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} -> {status} ({status_string(status)}): {msg}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so (built by ``python -m mixture_experts_ffn_08_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               f"`python -m mixture_experts_ffn_08_amd.build` (the HIP path has no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None,
+         optional: bool = False) -> int:
+    """Device address of a contiguous GPU tensor after checks (0 for an allowed None)."""
+    if t is None:
+        if optional:
+            return 0
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {numel} needed")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def moe_capacity(T: int, k: int, E: int, phi: Optional[float]) -> int:
+    """Capacity C = ceil(phi k T / E); -1 (dropless) for phi None."""
+    if phi is None:
+        return -1
+    return int(load().moe_capacity(T, k, E, float(phi)))
+
+
+def moe_permute_workspace_bytes(T: int, k: int, E: int) -> int:
+    return int(load().moe_permute_workspace_bytes(T, k, E))
+
+
+def moe_stats_workspace_bytes(T: int, E: int) -> int:
+    return int(load().moe_stats_workspace_bytes(T, E))
+
+
+def moe_route(x, w_router, logit_bias, T, d, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie,
+              stream=None):
+    dt = _dtype_code(x)
+    args = (_dev(x, "x", x.dtype, T * d), _dev(w_router, "w_router", x.dtype, E * d),
+            _dev(logit_bias, "logit_bias", torch.float32, E, optional=True), dt, T, d, E, k, mode,
+            int(bool(renorm)), _dev(logits, "logits", torch.float32, T * E),
+            _dev(topk_idx, "topk_idx", torch.int32, T * k), _dev(topk_w, "topk_w", torch.float32, T * k),
+            _dev(near_tie, "near_tie", torch.int32, T), _stream(stream))
+    _check("moe_route", load().moe_route(*args))
+
+
+def moe_permute(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm_token, x_perm, workspace,
+                stream=None):
+    dt = _dtype_code(x)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_dev(topk_idx, "topk_idx", torch.int32, T * k), T, k, E, int(capacity),
+            _dev(x, "x", x.dtype, T * d), dt, d, _dev(counts, "counts", torch.int32, E),
+            _dev(offsets, "offsets", torch.int32, E + 1), _dev(row_of, "row_of", torch.int32, T * k),
+            _dev(perm_token, "perm_token", torch.int32, T * k), _dev(x_perm, "x_perm", x.dtype, T * k * d),
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("moe_permute", load().moe_permute(*args))
+
+
+def moe_grouped_gate_up(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, a, stream=None):
+    dt = _dtype_code(x_perm)
+    args = (_dev(x_perm, "x_perm", x_perm.dtype, max_rows * d), _dev(offsets, "offsets", torch.int32, G + 1),
+            G, max_rows, d, F, _dev(w_gate, "w_gate", x_perm.dtype, G * F * d),
+            _dev(w_up, "w_up", x_perm.dtype, G * F * d), dt, _dev(a, "a", x_perm.dtype, max_rows * F),
+            _stream(stream))
+    _check("moe_grouped_gate_up", load().moe_grouped_gate_up(*args))
+
+
+def moe_grouped_down(a, offsets, G, max_rows, F, d, w_down, y_perm, stream=None):
+    dt = _dtype_code(a)
+    args = (_dev(a, "a", a.dtype, max_rows * F), _dev(offsets, "offsets", torch.int32, G + 1), G, max_rows,
+            F, d, _dev(w_down, "w_down", a.dtype, G * d * F), dt, _dev(y_perm, "y_perm", a.dtype, max_rows * d),
+            _stream(stream))
+    _check("moe_grouped_down", load().moe_grouped_down(*args))
+
+
+def moe_grouped_swiglu(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, w_down, a, y_perm, stream=None):
+    dt = _dtype_code(x_perm)
+    args = (_dev(x_perm, "x_perm", x_perm.dtype, max_rows * d), _dev(offsets, "offsets", torch.int32, G + 1),
+            G, max_rows, d, F, _dev(w_gate, "w_gate", x_perm.dtype, G * F * d),
+            _dev(w_up, "w_up", x_perm.dtype, G * F * d), _dev(w_down, "w_down", x_perm.dtype, G * d * F), dt,
+            _dev(a, "a", x_perm.dtype, max_rows * F), _dev(y_perm, "y_perm", x_perm.dtype, max_rows * d),
+            _stream(stream))
+    _check("moe_grouped_swiglu", load().moe_grouped_swiglu(*args))
+
+
+def moe_combine(y_perm, row_of, topk_w, shared_y, T, k, d, y, stream=None):
+    dt = _dtype_code(y)
+    args = (_dev(y_perm, "y_perm", y.dtype, T * k * d), _dev(row_of, "row_of", torch.int32, T * k),
+            _dev(topk_w, "topk_w", torch.float32, T * k),
+            _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), dt, T, k, d,
+            _dev(y, "y", y.dtype, T * d), _stream(stream))
+    _check("moe_combine", load().moe_combine(*args))
+
+
+def moe_stats(counts, logits, T, k, E, alpha, f, P, l_aux, max_over_mean, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_dev(counts, "counts", torch.int32, E), _dev(logits, "logits", torch.float32, T * E), T, k, E,
+            float(alpha), _dev(f, "f", torch.float32, E), _dev(P, "P", torch.float32, E),
+            _dev(l_aux, "l_aux", torch.float32, 1), _dev(max_over_mean, "max_over_mean", torch.float32, 1),
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("moe_stats", load().moe_stats(*args))

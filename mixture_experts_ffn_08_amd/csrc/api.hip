@@ -1,0 +1,274 @@
+// C ABI of libmoe.so (declared in include/moe.h): argument checks on the host,
+// then the kernel launchers.  Nothing is enqueued unless every check passes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+int elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+// Row width rule: multiples of 8 (fp32) or 128 (bf16).
+int width_check(const char* fn, const char* name, int v, int dt) {
+  if (v <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: %s = %d must be positive", fn, name, v);
+  const int m = dt == MOE_BF16 ? 128 : 8;
+  if (v % m != 0)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: %s = %d must be a multiple of %d for %s", fn, name, v, m,
+                dt == MOE_BF16 ? "bf16" : "fp32");
+  return MOE_OK;
+}
+
+int experts_check(const char* fn, int E, int k) {
+  if (E < 1 || E > MOE_MAX_EXPERTS)
+    return fail(E < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED, "%s: E = %d outside [1, %d]", fn, E,
+                MOE_MAX_EXPERTS);
+  if (k < 1 || k > E) return fail(MOE_ERR_INVALID_ARG, "%s: k = %d outside [1, E = %d]", fn, k, E);
+  return MOE_OK;
+}
+
+int assignments_check(const char* fn, int T, int k) {
+  if ((int64_t)T * k > INT32_MAX) return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld exceeds 2^31-1", fn,
+                                              (long long)T * k);
+  return MOE_OK;
+}
+
+#define CHECK(x)                  \
+  do {                            \
+    const int _s = (x);           \
+    if (_s != MOE_OK) return _s;  \
+  } while (0)
+#define NEED(p, fn)                                                                           \
+  do {                                                                                        \
+    if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: %s must not be NULL", fn, #p); \
+  } while (0)
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int64_t moe_capacity(int64_t T, int k, int E, double phi) {
+  if (!(phi >= 0.0) || isinf(phi) || T < 0 || k < 1 || E < 1) return -1;
+  // phi = m * 2^ex exactly, m an integer below 2^53.
+  int ex = 0;
+  const double fr = frexp(phi, &ex);
+  int64_t m = (int64_t)ldexp(fr, 53);
+  ex -= 53;
+  while (m != 0 && (m & 1) == 0) {
+    m >>= 1;
+    ++ex;
+  }
+  // C = ceil(m * 2^ex * T * k / E), in 128-bit integers.
+  __int128 num = (__int128)m * T * k;
+  __int128 den = E;
+  if (ex >= 0) {
+    if (ex > 40) return INT64_MAX;
+    num <<= ex;
+  } else {
+    if (-ex >= 120) return num == 0 ? 0 : 1;
+    den <<= -ex;
+  }
+  const __int128 c = (num + den - 1) / den;
+  return c > (__int128)INT64_MAX ? INT64_MAX : (int64_t)c;
+}
+
+size_t moe_permute_workspace_bytes(int T, int k, int E) {
+  if (T <= 0 || k < 1 || E < 1) return 0;
+  const size_t nblk = (size_t)moe::permute_blocks(T, k);
+  return 2 * round_up(nblk * (size_t)E * sizeof(int32_t), 256);
+}
+
+size_t moe_stats_workspace_bytes(int T, int E) {
+  if (T <= 0 || E < 1) return 0;
+  return round_up((size_t)moe::stats_blocks(T) * (size_t)E * sizeof(float), 256);
+}
+
+int moe_route(const void* x, const void* w_router, const float* logit_bias, int dtype, int T, int d, int E,
+              int k, int mode, int renorm, float* logits, int32_t* topk_idx, float* topk_w, int32_t* near_tie,
+              hipStream_t stream) {
+  static const char* fn = "moe_route";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (mode != MOE_SOFTMAX_THEN_TOPK && mode != MOE_TOPK_THEN_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARG, "%s: unknown score mode %d", fn, mode);
+  CHECK(experts_check(fn, E, k));
+  if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
+  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
+  CHECK(assignments_check(fn, T, k));
+  if (T == 0) return ok();
+  NEED(x, fn);
+  NEED(w_router, fn);
+  NEED(logits, fn);
+  NEED(topk_idx, fn);
+  NEED(topk_w, fn);
+  NEED(near_tie, fn);
+  moe::RouteArgs a{x, w_router, logit_bias, dtype, T, d, E, k, mode, renorm ? 1 : 0,
+                   logits, topk_idx, topk_w, near_tie};
+  return hip_status(moe::launch_route(a, stream), fn);
+}
+
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
+                int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token, void* x_perm,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "moe_permute";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  CHECK(experts_check(fn, E, k));
+  if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
+  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
+  CHECK(assignments_check(fn, T, k));
+  if (T == 0) return ok();
+  NEED(topk_idx, fn);
+  NEED(x, fn);
+  NEED(counts, fn);
+  NEED(offsets, fn);
+  NEED(row_of, fn);
+  NEED(perm_token, fn);
+  NEED(x_perm, fn);
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  const size_t half = need / 2;
+  moe::PermuteArgs a{topk_idx, T, k, E, capacity < 0 ? -1 : capacity, x, d * elem_bytes(dtype), counts,
+                     offsets, row_of, perm_token, x_perm, static_cast<int32_t*>(workspace),
+                     reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half)};
+  return hip_status(moe::launch_permute(a, stream), fn);
+}
+
+static int grouped_check(const char* fn, int G, int max_rows, int d, int F, int dtype) {
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (G < 1 || G > MOE_MAX_EXPERTS)
+    return fail(G < 1 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED, "%s: G = %d outside [1, %d]", fn, G,
+                MOE_MAX_EXPERTS);
+  if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "%s: max_rows = %d < 0", fn, max_rows);
+  CHECK(width_check(fn, "d", d, dtype));
+  CHECK(width_check(fn, "F", F, dtype));
+  return MOE_OK;
+}
+
+int moe_grouped_gate_up(const void* x_perm, const int32_t* offsets, int G, int max_rows, int d, int F,
+                        const void* w_gate, const void* w_up, int dtype, void* a, hipStream_t stream) {
+  static const char* fn = "moe_grouped_gate_up";
+  CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
+  if (max_rows == 0) return ok();
+  NEED(x_perm, fn);
+  NEED(offsets, fn);
+  NEED(w_gate, fn);
+  NEED(w_up, fn);
+  NEED(a, fn);
+  moe::GroupedGemmArgs g{x_perm, offsets, G, max_rows, F, d, w_gate, w_up, a, dtype};
+  return hip_status(moe::launch_grouped_gemm(g, true, stream), fn);
+}
+
+int moe_grouped_down(const void* a, const int32_t* offsets, int G, int max_rows, int F, int d,
+                     const void* w_down, int dtype, void* y_perm, hipStream_t stream) {
+  static const char* fn = "moe_grouped_down";
+  CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
+  if (max_rows == 0) return ok();
+  NEED(a, fn);
+  NEED(offsets, fn);
+  NEED(w_down, fn);
+  NEED(y_perm, fn);
+  moe::GroupedGemmArgs g{a, offsets, G, max_rows, d, F, w_down, nullptr, y_perm, dtype};
+  return hip_status(moe::launch_grouped_gemm(g, false, stream), fn);
+}
+
+int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int G, int max_rows, int d, int F,
+                       const void* w_gate, const void* w_up, const void* w_down, int dtype, void* a,
+                       void* y_perm, hipStream_t stream) {
+  static const char* fn = "moe_grouped_swiglu";
+  CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
+  if (max_rows == 0) return ok();
+  NEED(w_down, fn);
+  NEED(y_perm, fn);
+  CHECK(moe_grouped_gate_up(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, dtype, a, stream));
+  return moe_grouped_down(a, offsets, G, max_rows, F, d, w_down, dtype, y_perm, stream);
+}
+
+int moe_combine(const void* y_perm, const int32_t* row_of, const float* topk_w, const void* shared_y,
+                int dtype, int T, int k, int d, void* y, hipStream_t stream) {
+  static const char* fn = "moe_combine";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: k = %d < 1", fn, k);
+  if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
+  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
+  CHECK(assignments_check(fn, T, k));
+  if (T == 0) return ok();
+  NEED(y_perm, fn);
+  NEED(row_of, fn);
+  NEED(topk_w, fn);
+  NEED(y, fn);
+  moe::CombineArgs c{y_perm, row_of, topk_w, shared_y, dtype, T, k, d, y};
+  return hip_status(moe::launch_combine(c, stream), fn);
+}
+
+int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, float alpha, float* f, float* P,
+              float* l_aux, float* max_over_mean, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  static const char* fn = "moe_stats";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  CHECK(experts_check(fn, E, k));
+  CHECK(assignments_check(fn, T, k));
+  if (!isfinite(alpha)) return fail(MOE_ERR_INVALID_ARG, "%s: alpha is not finite", fn);
+  if (T == 0) return ok();
+  NEED(counts, fn);
+  NEED(logits, fn);
+  NEED(f, fn);
+  NEED(P, fn);
+  NEED(l_aux, fn);
+  NEED(max_over_mean, fn);
+  const size_t need = moe_stats_workspace_bytes(T, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  moe::StatsArgs s{counts, logits, T, k, E, alpha, f, P, l_aux, max_over_mean, static_cast<float*>(workspace)};
+  return hip_status(moe::launch_stats(s, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Device helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 32x32 output, K = 16 per instruction.  Lane l supplies A row (l % 32) and B
+// column (l % 32), each with the 8 k values 8*(l/32) .. 8*(l/32)+7.
+// Accumulator element i of lane l is row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16 output, K = 32 per instruction.  Lane l supplies A row (l % 16) and B
+// column (l % 16) with k values 8*(l/16) .. 8*(l/16)+7.  Accumulator element i
+// of lane l is row 4*(l/16) + i, column l % 16.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Butterfly exchange inside each 32-lane half through ds_swizzle (bit mode:
+// and-mask 0x1f, xor-mask X).
+template <int X>
+__device__ __forceinline__ uint32_t swz_xor(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (X << 10) | 0x1f);
+}
+template <int X>
+__device__ __forceinline__ float swz_xor(float v) {
+  return __uint_as_float(swz_xor<X>(__float_as_uint(v)));
+}
+
+// Sum over the wave; every lane gets the same value (same tree on every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += swz_xor<1>(v);
+  v += swz_xor<2>(v);
+  v += swz_xor<4>(v);
+  v += swz_xor<8>(v);
+  v += swz_xor<16>(v);
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  return a + b;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, swz_xor<1>(v));
+  v = fmaxf(v, swz_xor<2>(v));
+  v = fmaxf(v, swz_xor<4>(v));
+  v = fmaxf(v, swz_xor<8>(v));
+  v = fmaxf(v, swz_xor<16>(v));
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  return fmaxf(a, b);
+}
+
+// Total order on float32 scores as uint32: larger float -> larger key; -0 and +0
+// map to the same key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace moe

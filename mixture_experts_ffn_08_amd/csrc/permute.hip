@@ -1,0 +1,166 @@
+// Dispatch: per-expert histogram, capacity, stable permutation and row gather.
+//
+// ML Interview Notes, MoELayer listing: each expert collects the (token, slot)
+// pairs that chose it.  "Capacity factor" and Transformers & Math 17.5: an
+// expert holds at most C tokens, later arrivals are dropped by that expert.
+//
+// Assignments p = t*k + j arrive in ascending p.  The rank of p in its expert
+// is fixed by the data, not by atomics: block b (512 assignments) records which
+// of its assignments chose each expert in an LDS bitmap (atomicOr commutes, so
+// the bitmap is the same in any order); rank = (assignments of earlier blocks,
+// from a scan of per-block histograms) + popcount of the earlier bits.
+//
+//   hist_kernel   per-block expert histograms (LDS atomics)
+//   scan_kernel   one block: per-expert scan over blocks, demand counts,
+//                 capacity, exclusive scan over experts -> offsets
+//   rank_kernel   bitmap ranks -> row_of, perm_token
+//   gather_kernel x_perm[r] = x[perm_token[r]], one wave per row, 16-byte lanes
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBP = kPairsPerBlock;  // 512 threads, one assignment each
+constexpr int kWords = kBP / 32;     // bitmap words per expert
+
+__global__ __launch_bounds__(kBP) void hist_kernel(const int32_t* __restrict__ idx, int64_t P, int E,
+                                                    int32_t* __restrict__ block_counts) {
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kBP) cnt[e] = 0;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * kBP + tid;
+  if (p < P) {
+    const int e = idx[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kBP) block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One block of 1024 threads.  tpe threads per expert split the block list into
+// contiguous chunks; chunk sums are scanned in LDS, then each thread writes the
+// running base of its blocks.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
+                                                     int E, int tpe, int64_t cap,
+                                                     int32_t* __restrict__ block_base,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets) {
+  __shared__ int part[1024];
+  __shared__ int kept_s[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int e = tid / tpe, c = tid % tpe;
+  const int chunk = (nblk + tpe - 1) / tpe;
+  const int b0 = min(c * chunk, nblk), b1 = min(b0 + chunk, nblk);
+  const bool active = e < E;
+  int sum = 0;
+  if (active)
+    for (int b = b0; b < b1; ++b) sum += block_counts[(size_t)b * E + e];
+  part[tid] = sum;
+  __syncthreads();
+  if (active) {
+    int base = 0;
+    for (int q = 0; q < c; ++q) base += part[e * tpe + q];
+    for (int b = b0; b < b1; ++b) {
+      block_base[(size_t)b * E + e] = base;
+      base += block_counts[(size_t)b * E + e];
+    }
+    if (c == tpe - 1) {
+      counts[e] = base;
+      kept_s[e] = cap < 0 ? base : (int)min((int64_t)base, cap);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    offsets[0] = 0;
+    for (int q = 0; q < E; ++q) {
+      run += kept_s[q];
+      offsets[q + 1] = run;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ idx, int64_t P, int k, int E,
+                                                    int64_t cap, const int32_t* __restrict__ block_base,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ row_of,
+                                                    int32_t* __restrict__ perm_token) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kBP) mask[i] = 0u;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * kBP + tid;
+  const int e = p < P ? idx[p] : -1;
+  const bool valid = (unsigned)e < (unsigned)E;
+  const int w = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid) atomicOr(&mask[e * kWords + w], bit);
+  __syncthreads();
+  if (p >= P) return;
+  int32_t row = -1;
+  if (valid) {
+    const uint32_t* m = mask + e * kWords;
+    int r = __popc(m[w] & (bit - 1u));
+    for (int q = 0; q < w; ++q) r += __popc(m[q]);
+    const int rank = block_base[(size_t)blockIdx.x * E + e] + r;
+    if (cap < 0 || rank < cap) {
+      row = offsets[e] + rank;
+      perm_token[row] = (int32_t)(p / k);
+    }
+  }
+  row_of[p] = row;
+}
+
+__global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
+                                                      const int32_t* __restrict__ perm_token,
+                                                      const int32_t* __restrict__ offsets_end, int T,
+                                                      int max_rows, int row_bytes, char* __restrict__ x_perm) {
+  const int R = min(*offsets_end, max_rows);
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nwaves = gridDim.x * 4;
+  for (int r = wave; r < R; r += nwaves) {
+    const int t = perm_token[r];
+    if ((unsigned)t >= (unsigned)T) continue;
+    const char* src = x + (size_t)t * row_bytes;
+    char* dst = x_perm + (size_t)r * row_bytes;
+    int off = lane * 16;
+    // four 16-byte loads in flight per lane, then their stores
+    for (; off + 3 * 1024 < row_bytes; off += 4 * 1024) {
+      const u32x4 v0 = ld16(src + off), v1 = ld16(src + off + 1024);
+      const u32x4 v2 = ld16(src + off + 2048), v3 = ld16(src + off + 3072);
+      st16(dst + off, v0);
+      st16(dst + off + 1024, v1);
+      st16(dst + off + 2048, v2);
+      st16(dst + off + 3072, v3);
+    }
+    for (; off < row_bytes; off += 1024) st16(dst + off, ld16(src + off));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
+  const int64_t P = (int64_t)a.T * a.k;
+  const int nblk = permute_blocks(a.T, a.k);
+  int ep = 1;
+  while (ep < a.E) ep <<= 1;
+  const int tpe = min(64, 1024 / ep);
+  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, tpe,
+                     a.capacity, a.block_base, a.counts, a.offsets);
+  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
+                     a.block_base, a.offsets, a.row_of, a.perm_token);
+  const int max_rows = (int)P;
+  const int blocks = (int)std::min<int64_t>((max_rows + 3) / 4, 8192);
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
+                     (const char*)a.x, a.perm_token, a.offsets + a.E, a.T, max_rows, a.row_bytes,
+                     (char*)a.x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

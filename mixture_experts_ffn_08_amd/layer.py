@@ -1,0 +1,154 @@
+"""One MoE feed-forward layer on the GPU: device-resident weights and buffers,
+and the forward pass as a chain of libmoe.so calls on one stream.
+
+    route -> permute -> grouped gate/up -> grouped down -> [shared expert]
+          -> combine -> stats
+
+PyTorch only allocates device memory and supplies the stream; every step runs
+in the library's HIP kernels.  Nothing is read back to the host inside
+``forward``: grid sizes use the upper bound T*k rows.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from .inputs import LayerInputs, LayerShape
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Copy a host array (bf16 bit patterns as uint16, or float32) to the GPU."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+class DeviceWeights:
+    """Router, routed experts and shared expert of one layer in GPU memory.
+
+    gate/up [E][F][d], down [E][d][F] (nn.Linear order, per expert)."""
+
+    def __init__(self, inputs: LayerInputs, device="cuda"):
+        s = inputs.shape
+        self.shape, self.device = s, torch.device(device)
+        td = torch_dtype(s.dtype)
+        self.w_router = to_device(inputs.w_router, s.dtype, self.device)
+        self.bias = None if inputs.bias is None else torch.from_numpy(inputs.bias).to(self.device)
+        self.gate = torch.empty((s.E, s.F, s.d), dtype=td, device=self.device)
+        self.up = torch.empty((s.E, s.F, s.d), dtype=td, device=self.device)
+        self.down = torch.empty((s.E, s.d, s.F), dtype=td, device=self.device)
+
+        def sink(e, g, u, dn):
+            self.gate[e].copy_(to_device(g, s.dtype, self.device))
+            self.up[e].copy_(to_device(u, s.dtype, self.device))
+            self.down[e].copy_(to_device(dn, s.dtype, self.device))
+
+        inputs.experts(sink=sink)
+        sh = inputs.shared()
+        self.shared = None if sh is None else tuple(to_device(m, s.dtype, self.device) for m in sh)
+        torch.cuda.synchronize(self.device)
+
+
+class Buffers:
+    """Every intermediate and output of the layer for T tokens (device memory)."""
+
+    def __init__(self, shape: LayerShape, T: int, device="cuda"):
+        s = shape
+        dev = torch.device(device)
+        td = torch_dtype(s.dtype)
+        R = T * s.k
+        i32, f32 = torch.int32, torch.float32
+        self.T = T
+        self.logits = torch.empty((T, s.E), dtype=f32, device=dev)
+        self.topk_idx = torch.empty((T, s.k), dtype=i32, device=dev)
+        self.topk_w = torch.empty((T, s.k), dtype=f32, device=dev)
+        self.near_tie = torch.empty((T,), dtype=i32, device=dev)
+        self.counts = torch.empty((s.E,), dtype=i32, device=dev)
+        self.offsets = torch.empty((s.E + 1,), dtype=i32, device=dev)
+        self.row_of = torch.empty((T, s.k), dtype=i32, device=dev)
+        self.perm_token = torch.empty((max(R, 1),), dtype=i32, device=dev)
+        self.x_perm = torch.empty((max(R, 1), s.d), dtype=td, device=dev)
+        self.a = torch.empty((max(R, 1), s.F), dtype=td, device=dev)
+        self.y_perm = torch.empty((max(R, 1), s.d), dtype=td, device=dev)
+        self.y = torch.empty((T, s.d), dtype=td, device=dev)
+        self.f = torch.empty((s.E,), dtype=f32, device=dev)
+        self.P = torch.empty((s.E,), dtype=f32, device=dev)
+        self.l_aux = torch.empty((1,), dtype=f32, device=dev)
+        self.max_over_mean = torch.empty((1,), dtype=f32, device=dev)
+        self.ws_permute = torch.empty((max(_lib.moe_permute_workspace_bytes(T, s.k, s.E), 1),), dtype=torch.uint8,
+                                      device=dev)
+        self.ws_stats = torch.empty((max(_lib.moe_stats_workspace_bytes(T, s.E), 1),), dtype=torch.uint8,
+                                    device=dev)
+        if s.F_shared > 0:
+            self.shared_offsets = torch.tensor([0, T], dtype=i32, device=dev)
+            self.shared_a = torch.empty((max(T, 1), s.F_shared), dtype=td, device=dev)
+            self.shared_y = torch.empty((max(T, 1), s.d), dtype=td, device=dev)
+        else:
+            self.shared_offsets = self.shared_a = self.shared_y = None
+
+
+class MoeLayer:
+    """Forward pass of one MoE layer through libmoe.so."""
+
+    def __init__(self, weights: DeviceWeights):
+        self.w = weights
+        self.shape = weights.shape
+
+    def buffers(self, T: int) -> Buffers:
+        return Buffers(self.shape, T, self.w.device)
+
+    def route(self, x, b: Buffers, stream=None):
+        s = self.shape
+        _lib.moe_route(x, self.w.w_router, self.w.bias, b.T, s.d, s.E, s.k, s.mode, s.renorm, b.logits,
+                       b.topk_idx, b.topk_w, b.near_tie, stream)
+
+    def permute(self, x, b: Buffers, stream=None):
+        s = self.shape
+        cap = _lib.moe_capacity(b.T, s.k, s.E, s.phi)
+        _lib.moe_permute(b.topk_idx, b.T, s.k, s.E, cap, x, s.d, b.counts, b.offsets, b.row_of, b.perm_token,
+                         b.x_perm, b.ws_permute, stream)
+
+    def experts(self, b: Buffers, stream=None):
+        s = self.shape
+        R = b.T * s.k
+        _lib.moe_grouped_gate_up(b.x_perm, b.offsets, s.E, R, s.d, s.F, self.w.gate, self.w.up, b.a, stream)
+        _lib.moe_grouped_down(b.a, b.offsets, s.E, R, s.F, s.d, self.w.down, b.y_perm, stream)
+
+    def shared_expert(self, x, b: Buffers, stream=None):
+        s = self.shape
+        if self.w.shared is None:
+            return
+        g, u, dn = self.w.shared
+        _lib.moe_grouped_swiglu(x, b.shared_offsets, 1, b.T, s.d, s.F_shared, g, u, dn, b.shared_a, b.shared_y,
+                                stream)
+
+    def combine(self, b: Buffers, stream=None):
+        s = self.shape
+        _lib.moe_combine(b.y_perm, b.row_of, b.topk_w, b.shared_y, b.T, s.k, s.d, b.y, stream)
+
+    def stats(self, b: Buffers, stream=None):
+        s = self.shape
+        _lib.moe_stats(b.counts, b.logits, b.T, s.k, s.E, s.alpha, b.f, b.P, b.l_aux, b.max_over_mean,
+                       b.ws_stats, stream)
+
+    def forward(self, x: torch.Tensor, b: Optional[Buffers] = None, stream=None) -> Buffers:
+        """Whole layer for x[T][d] (device).  Returns the buffers holding y and
+        every intermediate; asynchronous on `stream`."""
+        if b is None:
+            b = self.buffers(x.shape[0])
+        if b.T == 0:
+            return b
+        self.route(x, b, stream)
+        self.permute(x, b, stream)
+        self.experts(b, stream)
+        self.shared_expert(x, b, stream)
+        self.combine(b, stream)
+        self.stats(b, stream)
+        return b

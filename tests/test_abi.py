@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/moe.h declares, and rejects bad arguments on the host before any
+launch.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from mixture_experts_ffn_08_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_stats"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+@pytest.mark.parametrize("T,k,E,phi", [(4096, 8, 64, 1.25), (4096, 2, 8, 1.25), (64, 2, 8, 1.0), (63, 2, 8, 1.0),
+                                       (10, 1, 1, 0.3), (10, 1, 1, 1.1), (1000, 3, 7, 1.7), (5, 5, 5, 0.0),
+                                       (123457, 8, 256, 0.9999), (16384, 8, 128, 2.5)])
+def test_capacity_matches_oracle(T, k, E, phi):
+    assert _lib.moe_capacity(T, k, E, phi) == oracle.capacity(T, k, E, phi)
+
+
+def test_capacity_dropless_and_invalid():
+    lib = _lib.load()
+    assert _lib.moe_capacity(10, 1, 1, None) == -1
+    assert lib.moe_capacity(10, 1, 1, float("nan")) == -1
+    assert lib.moe_capacity(10, 1, 1, float("inf")) == -1
+    assert lib.moe_capacity(10, 1, 1, -1.0) == -1
+    assert lib.moe_capacity(10, 0, 1, 1.0) == -1
+
+
+def test_workspace_sizes():
+    assert _lib.moe_permute_workspace_bytes(16384, 8, 128) >= 2 * (16384 * 8 // 512) * 128 * 4
+    assert _lib.moe_permute_workspace_bytes(0, 8, 128) == 0
+    assert _lib.moe_stats_workspace_bytes(16384, 128) >= (16384 // 64) * 128 * 4
+    assert _lib.moe_stats_workspace_bytes(0, 128) == 0
+
+
+def test_status_strings():
+    for code, name in [(0, "MOE_OK"), (-1, "MOE_ERR_INVALID_ARG"), (-2, "MOE_ERR_UNSUPPORTED"),
+                       (-3, "MOE_ERR_WORKSPACE"), (-4, "MOE_ERR_HIP"), (7, "MOE_ERR_UNKNOWN")]:
+        assert _lib.status_string(code) == name
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def route(**kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, dtype=1, T=4, d=128, E=8, k=2, mode=0, renorm=1, logits=FAKE,
+             idx=FAKE, w_out=FAKE, near=FAKE)
+    a.update(kw)
+    return _lib.load().moe_route(a["x"], a["w"], a["bias"], a["dtype"], a["T"], a["d"], a["E"], a["k"],
+                                 a["mode"], a["renorm"], a["logits"], a["idx"], a["w_out"], a["near"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), -1), (dict(dtype=7), -1), (dict(mode=2), -1), (dict(E=0), -1), (dict(E=257), -2),
+    (dict(k=0), -1), (dict(k=9), -1), (dict(d=0), -1), (dict(d=12), -2), (dict(x=None), -1),
+    (dict(w=None), -1), (dict(logits=None), -1), (dict(idx=None), -1), (dict(w_out=None), -1),
+    (dict(near=None), -1), (dict(T=2 ** 30, k=4), -2),
+])
+def test_route_rejects_before_launch(kw, status):
+    assert route(**kw) == status
+    assert _lib.last_error()
+
+
+def test_route_zero_tokens_is_a_no_op():
+    assert route(T=0, x=None, w=None, logits=None, idx=None, w_out=None, near=None) == 0
+    assert _lib.last_error() == ""
+
+
+def permute(**kw):
+    a = dict(idx=FAKE, T=4, k=2, E=8, cap=-1, x=FAKE, dtype=1, d=128, counts=FAKE, offsets=FAKE, row_of=FAKE,
+             perm=FAKE, x_perm=FAKE, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return _lib.load().moe_permute(a["idx"], a["T"], a["k"], a["E"], a["cap"], a["x"], a["dtype"], a["d"],
+                                   a["counts"], a["offsets"], a["row_of"], a["perm"], a["x_perm"], a["ws"],
+                                   a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-3), -1), (dict(dtype=3), -1), (dict(k=9), -1), (dict(d=4), -2), (dict(idx=None), -1),
+    (dict(x_perm=None), -1), (dict(ws=None), -3), (dict(ws_bytes=8), -3), (dict(counts=None), -1),
+])
+def test_permute_rejects_before_launch(kw, status):
+    assert permute(**kw) == status
+
+
+def test_permute_zero_tokens_is_a_no_op():
+    assert permute(T=0, idx=None, ws=None, ws_bytes=0) == 0
+
+
+def gate_up(**kw):
+    a = dict(xp=FAKE, off=FAKE, G=8, rows=16, d=256, F=384, wg=FAKE, wu=FAKE, dtype=1, out=FAKE)
+    a.update(kw)
+    return _lib.load().moe_grouped_gate_up(a["xp"], a["off"], a["G"], a["rows"], a["d"], a["F"], a["wg"],
+                                           a["wu"], a["dtype"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(G=0), -1), (dict(G=300), -2), (dict(rows=-1), -1), (dict(d=200), -2), (dict(F=136), -2),
+    (dict(dtype=0, d=12), -2), (dict(dtype=9), -1), (dict(wg=None), -1), (dict(out=None), -1),
+])
+def test_grouped_rejects_before_launch(kw, status):
+    assert gate_up(**kw) == status
+
+
+def test_grouped_zero_rows_is_a_no_op():
+    assert gate_up(rows=0, xp=None, off=None, wg=None, wu=None, out=None) == 0
+    lib = _lib.load()
+    assert lib.moe_grouped_swiglu(None, None, 4, 0, 256, 256, None, None, None, 1, None, None, None) == 0
+    assert lib.moe_grouped_down(None, FAKE, 4, 8, 256, 256, FAKE, 1, FAKE, None) == -1
+
+
+def test_combine_and_stats_reject_before_launch():
+    lib = _lib.load()
+    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, -1, 2, 128, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, 4, 0, 128, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, 4, 2, 12, FAKE, None) == -2
+    assert lib.moe_combine(None, FAKE, FAKE, None, 1, 4, 2, 128, FAKE, None) == -1
+    assert lib.moe_combine(None, None, None, None, 1, 0, 2, 128, None, None) == 0
+    assert lib.moe_stats(FAKE, FAKE, 4, 2, 8, 0.01, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -3
+    assert lib.moe_stats(FAKE, FAKE, 4, 9, 8, 0.01, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.moe_stats(FAKE, FAKE, 4, 2, 8, float("nan"), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.moe_stats(None, None, 0, 2, 8, 0.01, None, None, None, None, None, 0, None) == 0

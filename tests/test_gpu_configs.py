@@ -1,0 +1,88 @@
+"""GPU parity on the full-size layers (Mixtral-, Qwen2-, Qwen3- and
+DeepSeek-V3-shaped, plus the tiny fp32 layer), in the launch configuration the
+benchmark times.  Routing, dispatch and statistics are compared in full
+(the oracle routes every token); expert outputs on sampled permuted rows; the
+layer output on sampled tokens, computed one by one from the definition."""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_ffn_08_amd import inputs as minp
+from support import TOL, ExpertCache, GpuRun, check_dispatch, check_route, check_stats, host, log, oracle_route
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = ["tiny_f32", "mixtral", "mixtral_cap", "qwen2", "qwen3_prefill", "qwen3_decode", "dsv3_skew"]
+
+
+def sample_rows(offsets, rng, max_experts=6, per_expert=4):
+    """A few permuted rows (first, last, random) of a few non-empty experts."""
+    nonempty = np.nonzero(np.diff(offsets) > 0)[0]
+    chosen = rng.choice(nonempty, size=min(max_experts, len(nonempty)), replace=False)
+    rows = []
+    for e in sorted(chosen):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        cand = {lo, hi - 1} | set(rng.integers(lo, hi, size=per_expert - 2).tolist())
+        rows += [(int(e), r) for r in sorted(cand)]
+    return rows
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_config_parity(name):
+    shape = minp.SHAPES[name]
+    rng = np.random.default_rng(1234)
+    t0 = time.time()
+    inp = minp.LayerInputs(shape, seed=0)
+    run = GpuRun(inp)
+    try:
+        out = run.run()
+        b = run.bufs
+        log(f"[{name}] GPU layer done at {time.time() - t0:.1f}s")
+        ref = oracle_route(inp)
+        tie = check_route(inp, out, ref)
+        counts, offsets, row_of, perm_token = check_dispatch(inp, out)
+        check_stats(inp, out)
+        cap = oracle.capacity(shape.T, shape.k, shape.E, shape.phi)
+        _, _, row_ref, _ = oracle.dispatch(ref[1], shape.E, cap)   # the oracle's own routing
+        if shape.phi is not None:
+            # dropped set: the same as the oracle's when no near tie flips a token
+            dropped_gpu = set(map(tuple, np.argwhere(out["row_of"] < 0).tolist()))
+            dropped_ref = set(map(tuple, np.argwhere(row_ref < 0).tolist()))
+            if not tie.any():
+                assert dropped_gpu == dropped_ref
+            log(f"[{name}] capacity {cap}: {len(dropped_gpu)} dropped assignments (oracle routing: {len(dropped_ref)})")
+        xs = minp.as_f32(inp.x, shape.dtype)
+        ex = ExpertCache(inp)
+        tol = TOL[shape.dtype]
+        # permuted rows: gather exact, gate/up and down within tolerance
+        rows = sample_rows(offsets, rng)
+        x_perm = host(b.x_perm[[r for _, r in rows]])
+        a_gpu = host(b.a[[r for _, r in rows]])
+        y_gpu = host(b.y_perm[[r for _, r in rows]])
+        assert np.array_equal(x_perm, xs[perm_token[[r for _, r in rows]]])
+        a_err = y_err = 0.0
+        for i, (e, r) in enumerate(rows):
+            g, u, dn = ex(e)
+            a_ref = oracle.swiglu_hidden(x_perm[i:i + 1], g, u)[0]
+            y_ref = (a_ref[None, :] @ dn.astype(np.float64).T)[0]
+            a_err = max(a_err, np.abs(a_gpu[i] - a_ref).max() / np.abs(a_ref).max())
+            y_err = max(y_err, np.abs(y_gpu[i] - y_ref).max() / np.abs(y_ref).max())
+        log(f"[{name}] expert rows: {len(rows)} sampled, max rel err a {a_err:.2e}, y_perm {y_err:.2e}")
+        assert a_err <= tol and y_err <= tol
+        # layer output on sampled tokens, straight from the definition
+        sh = ex.shared()
+        same_kept = ((out["row_of"] >= 0) == (row_ref >= 0)).all(1)
+        cand = np.nonzero(~tie & same_kept)[0]
+        toks = sorted(set(rng.choice(cand, size=min(6, len(cand)), replace=False).tolist()) | {int(cand[0]), int(cand[-1])})
+        err = ymax = 0.0
+        for t in toks:
+            y_ref = oracle.token_output(xs[t], ref[1][t], ref[2][t], row_ref[t] >= 0, ex, sh)
+            err = max(err, float(np.abs(out["y"][t] - y_ref).max()))
+            ymax = max(ymax, float(np.abs(y_ref).max()))
+        log(f"[{name}] end-to-end on {len(toks)} tokens: max|dy|/max|y| = {err / ymax:.3e} (tol {tol}); "
+            f"total {time.time() - t0:.1f}s")
+        assert err <= tol * ymax
+    finally:
+        run.free()
