@@ -42,21 +42,15 @@ def parse():
 
 def timed_steps(layer, x, bufs, steps, warmup, stream, torch):
     """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down)."""
-    from mixture_experts_ffn_08_amd import _lib
-
-    s = layer.shape
-    R = bufs.T * s.k
-
     def step(ev=None):
         layer.route(x, bufs, stream)
         layer.permute(x, bufs, stream)
         if ev is not None:
             ev[0].record(stream)
-        _lib.moe_grouped_gate_up(bufs.x_perm, bufs.offsets, s.E, R, s.d, s.F, layer.w.gate, layer.w.up, bufs.a,
-                                 stream)
+        layer.gate_up(x, bufs, stream)
         if ev is not None:
             ev[1].record(stream)
-        _lib.moe_grouped_down(bufs.a, bufs.offsets, s.E, R, s.F, s.d, layer.w.down, bufs.y_perm, stream)
+        layer.down(bufs, stream)
         if ev is not None:
             ev[2].record(stream)
         layer.shared_expert(x, bufs, stream)

@@ -112,7 +112,10 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, int 
  *   perm_token device [T*k] int32 out     token of each row; rows >= offsets[E]
  *                                        are left untouched
  *   x_perm     device [T*k][d] dtype out  x_perm[r] = x[perm_token[r]] for
- *                                        r < offsets[E]
+ *                                        r < offsets[E]; may be NULL (then x may
+ *                                        be NULL too): no copy is made, and the
+ *                                        expert GEMM gathers rows through
+ *                                        perm_token instead (row_index below)
  *   workspace  device, >= moe_permute_workspace_bytes(T, k, E) bytes, scratch
  */
 int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity,
@@ -133,12 +136,18 @@ int64_t moe_capacity(int64_t T, int k, int E, double phi);
 /*
  * moe_grouped_gate_up -- first half of G SwiGLU experts as one variable-size
  * grouped GEMM: for each group g and each row r in [offsets[g], offsets[g+1]),
- *     a[r] = SiLU(x_perm[r] gate[g]^T) * (x_perm[r] up[g]^T),  SiLU(z) = z/(1+e^-z)
+ *     a[r] = SiLU(h_r gate[g]^T) * (h_r up[g]^T),  SiLU(z) = z/(1+e^-z)
+ * where h_r = x[r], or h_r = x[row_index[r]] when row_index is given.
  * Sources: The Residual Stream, "An MoE tiny GPT" listing (F.silu(h @ gate) *
  * (h @ up)); ML Interview Notes "Capacity factor" (dropless routing with
  * variable-size grouped GEMMs).
  *
- *   x_perm   device [max_rows][d] dtype
+ *   x        device [max_rows][d] dtype (row_index NULL) or [src_rows][d]
+ *   row_index device [max_rows] int32 or NULL: the dispatch permutation
+ *                                        (perm_token of moe_permute), values
+ *                                        clamped to [0, src_rows); lets the GEMM
+ *                                        gather token rows itself
+ *   src_rows number of rows of x when row_index is given (ignored otherwise)
  *   offsets  device [G+1] int32           group row ranges; values are clamped to
  *                                        [0, max_rows]; rows outside every range
  *                                        are not written
@@ -147,7 +156,8 @@ int64_t moe_capacity(int64_t T, int k, int E, double phi);
  * G in [1, 256].  max_rows >= 0 bounds the launch; the true row count is read
  * from offsets on the device, so no host round trip is needed.
  */
-int moe_grouped_gate_up(const void* x_perm, const int32_t* offsets, int G, int max_rows,
+int moe_grouped_gate_up(const void* x, const int32_t* row_index, int src_rows,
+                        const int32_t* offsets, int G, int max_rows,
                         int d, int F, const void* w_gate, const void* w_up, int dtype,
                         void* a, hipStream_t stream);
 
@@ -164,10 +174,12 @@ int moe_grouped_down(const void* a, const int32_t* offsets, int G, int max_rows,
 /*
  * moe_grouped_swiglu -- moe_grouped_gate_up then moe_grouped_down: G SwiGLU
  * experts (SiLU(h gate^T) * (h up^T)) down^T over their row groups.  The shared
- * expert of a layer is this call with G = 1, offsets = {0, T} and x as x_perm
- * (Transformers & Math 17.3; ML Interview Notes, MoELayer, always-on experts).
+ * expert of a layer is this call with G = 1, offsets = {0, T}, x the tokens and
+ * no row index (Transformers & Math 17.3; ML Interview Notes, MoELayer,
+ * always-on experts).
  */
-int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int G, int max_rows,
+int moe_grouped_swiglu(const void* x, const int32_t* row_index, int src_rows,
+                       const int32_t* offsets, int G, int max_rows,
                        int d, int F, const void* w_gate, const void* w_up,
                        const void* w_down, int dtype, void* a, void* y_perm,
                        hipStream_t stream);

@@ -34,9 +34,9 @@ _SIGS = {
     "moe_permute": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_capacity": (_I64, [_I64, _I, _I, ctypes.c_double]),
-    "moe_grouped_gate_up": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
+    "moe_grouped_gate_up": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "moe_grouped_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
-    "moe_grouped_swiglu": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P]),
+    "moe_grouped_swiglu": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P]),
     "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_stats": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_stats_workspace_bytes": (_SZ, [_I, _I]),
@@ -145,21 +145,31 @@ def moe_route(x, w_router, logit_bias, T, d, E, k, mode, renorm, logits, topk_id
 
 def moe_permute(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm_token, x_perm, workspace,
                 stream=None):
+    """x_perm None: no gathered copy (the gate/up GEMM reads x through perm_token)."""
     dt = _dtype_code(x)
     ws_bytes = workspace.numel() * workspace.element_size()
     args = (_dev(topk_idx, "topk_idx", torch.int32, T * k), T, k, E, int(capacity),
             _dev(x, "x", x.dtype, T * d), dt, d, _dev(counts, "counts", torch.int32, E),
             _dev(offsets, "offsets", torch.int32, E + 1), _dev(row_of, "row_of", torch.int32, T * k),
-            _dev(perm_token, "perm_token", torch.int32, T * k), _dev(x_perm, "x_perm", x.dtype, T * k * d),
+            _dev(perm_token, "perm_token", torch.int32, T * k),
+            _dev(x_perm, "x_perm", x.dtype, T * k * d, optional=True),
             _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     _check("moe_permute", load().moe_permute(*args))
 
 
-def moe_grouped_gate_up(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, a, stream=None):
-    dt = _dtype_code(x_perm)
-    args = (_dev(x_perm, "x_perm", x_perm.dtype, max_rows * d), _dev(offsets, "offsets", torch.int32, G + 1),
-            G, max_rows, d, F, _dev(w_gate, "w_gate", x_perm.dtype, G * F * d),
-            _dev(w_up, "w_up", x_perm.dtype, G * F * d), dt, _dev(a, "a", x_perm.dtype, max_rows * F),
+def _rows_args(x, row_index, src_rows, max_rows, d):
+    if row_index is None:
+        return _dev(x, "x", x.dtype, max_rows * d), 0, 0
+    return (_dev(x, "x", x.dtype, src_rows * d), _dev(row_index, "row_index", torch.int32, max_rows),
+            int(src_rows))
+
+
+def moe_grouped_gate_up(x, row_index, src_rows, offsets, G, max_rows, d, F, w_gate, w_up, a, stream=None):
+    """row_index None: row r reads x[r]; else x[row_index[r]] (x has src_rows rows)."""
+    dt = _dtype_code(x)
+    args = (*_rows_args(x, row_index, src_rows, max_rows, d), _dev(offsets, "offsets", torch.int32, G + 1),
+            G, max_rows, d, F, _dev(w_gate, "w_gate", x.dtype, G * F * d),
+            _dev(w_up, "w_up", x.dtype, G * F * d), dt, _dev(a, "a", x.dtype, max_rows * F),
             _stream(stream))
     _check("moe_grouped_gate_up", load().moe_grouped_gate_up(*args))
 
@@ -172,12 +182,13 @@ def moe_grouped_down(a, offsets, G, max_rows, F, d, w_down, y_perm, stream=None)
     _check("moe_grouped_down", load().moe_grouped_down(*args))
 
 
-def moe_grouped_swiglu(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, w_down, a, y_perm, stream=None):
-    dt = _dtype_code(x_perm)
-    args = (_dev(x_perm, "x_perm", x_perm.dtype, max_rows * d), _dev(offsets, "offsets", torch.int32, G + 1),
-            G, max_rows, d, F, _dev(w_gate, "w_gate", x_perm.dtype, G * F * d),
-            _dev(w_up, "w_up", x_perm.dtype, G * F * d), _dev(w_down, "w_down", x_perm.dtype, G * d * F), dt,
-            _dev(a, "a", x_perm.dtype, max_rows * F), _dev(y_perm, "y_perm", x_perm.dtype, max_rows * d),
+def moe_grouped_swiglu(x, row_index, src_rows, offsets, G, max_rows, d, F, w_gate, w_up, w_down, a, y_perm,
+                       stream=None):
+    dt = _dtype_code(x)
+    args = (*_rows_args(x, row_index, src_rows, max_rows, d), _dev(offsets, "offsets", torch.int32, G + 1),
+            G, max_rows, d, F, _dev(w_gate, "w_gate", x.dtype, G * F * d),
+            _dev(w_up, "w_up", x.dtype, G * F * d), _dev(w_down, "w_down", x.dtype, G * d * F), dt,
+            _dev(a, "a", x.dtype, max_rows * F), _dev(y_perm, "y_perm", x.dtype, max_rows * d),
             _stream(stream))
     _check("moe_grouped_swiglu", load().moe_grouped_swiglu(*args))
 

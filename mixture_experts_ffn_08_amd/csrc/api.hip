@@ -163,12 +163,11 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, 
   CHECK(assignments_check(fn, T, k));
   if (T == 0) return ok();
   NEED(topk_idx, fn);
-  NEED(x, fn);
   NEED(counts, fn);
   NEED(offsets, fn);
   NEED(row_of, fn);
   NEED(perm_token, fn);
-  NEED(x_perm, fn);
+  if (x_perm != nullptr) NEED(x, fn);
   const size_t need = moe_permute_workspace_bytes(T, k, E);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
@@ -188,20 +187,31 @@ static int grouped_check(const char* fn, int G, int max_rows, int d, int F, int 
   if (max_rows < 0) return fail(MOE_ERR_INVALID_ARG, "%s: max_rows = %d < 0", fn, max_rows);
   CHECK(width_check(fn, "d", d, dtype));
   CHECK(width_check(fn, "F", F, dtype));
+  // the bf16 kernel addresses each operand (rows x width, one expert's weights)
+  // with 32-bit byte offsets
+  const int64_t eb = elem_bytes(dtype), lim = (int64_t)UINT32_MAX;
+  if ((int64_t)max_rows * d * eb > lim || (int64_t)max_rows * F * eb > lim || (int64_t)d * F * eb > lim)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: an operand exceeds 4 GiB (max_rows=%d d=%d F=%d)", fn, max_rows, d, F);
   return MOE_OK;
 }
 
-int moe_grouped_gate_up(const void* x_perm, const int32_t* offsets, int G, int max_rows, int d, int F,
-                        const void* w_gate, const void* w_up, int dtype, void* a, hipStream_t stream) {
+int moe_grouped_gate_up(const void* x, const int32_t* row_index, int src_rows, const int32_t* offsets, int G,
+                        int max_rows, int d, int F, const void* w_gate, const void* w_up, int dtype, void* a,
+                        hipStream_t stream) {
   static const char* fn = "moe_grouped_gate_up";
   CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
+  if (row_index != nullptr && src_rows < 1)
+    return fail(MOE_ERR_INVALID_ARG, "%s: src_rows = %d must be positive with a row index", fn, src_rows);
+  if (row_index != nullptr && (int64_t)src_rows * d * elem_bytes(dtype) > (int64_t)UINT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: x exceeds 4 GiB (src_rows=%d d=%d)", fn, src_rows, d);
   if (max_rows == 0) return ok();
-  NEED(x_perm, fn);
+  NEED(x, fn);
   NEED(offsets, fn);
   NEED(w_gate, fn);
   NEED(w_up, fn);
   NEED(a, fn);
-  moe::GroupedGemmArgs g{x_perm, offsets, G, max_rows, F, d, w_gate, w_up, a, dtype};
+  moe::GroupedGemmArgs g{x, row_index, row_index ? src_rows : max_rows, offsets, G, max_rows, F, d,
+                         w_gate, w_up, a, dtype};
   return hip_status(moe::launch_grouped_gemm(g, true, stream), fn);
 }
 
@@ -214,19 +224,20 @@ int moe_grouped_down(const void* a, const int32_t* offsets, int G, int max_rows,
   NEED(offsets, fn);
   NEED(w_down, fn);
   NEED(y_perm, fn);
-  moe::GroupedGemmArgs g{a, offsets, G, max_rows, d, F, w_down, nullptr, y_perm, dtype};
+  moe::GroupedGemmArgs g{a, nullptr, max_rows, offsets, G, max_rows, d, F, w_down, nullptr, y_perm, dtype};
   return hip_status(moe::launch_grouped_gemm(g, false, stream), fn);
 }
 
-int moe_grouped_swiglu(const void* x_perm, const int32_t* offsets, int G, int max_rows, int d, int F,
-                       const void* w_gate, const void* w_up, const void* w_down, int dtype, void* a,
-                       void* y_perm, hipStream_t stream) {
+int moe_grouped_swiglu(const void* x, const int32_t* row_index, int src_rows, const int32_t* offsets, int G,
+                       int max_rows, int d, int F, const void* w_gate, const void* w_up, const void* w_down,
+                       int dtype, void* a, void* y_perm, hipStream_t stream) {
   static const char* fn = "moe_grouped_swiglu";
   CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
   if (max_rows == 0) return ok();
   NEED(w_down, fn);
   NEED(y_perm, fn);
-  CHECK(moe_grouped_gate_up(x_perm, offsets, G, max_rows, d, F, w_gate, w_up, dtype, a, stream));
+  CHECK(moe_grouped_gate_up(x, row_index, src_rows, offsets, G, max_rows, d, F, w_gate, w_up, dtype, a,
+                            stream));
   return moe_grouped_down(a, offsets, G, max_rows, F, d, w_down, dtype, y_perm, stream);
 }
 

@@ -6,8 +6,10 @@
 // Transformers & Math 17.5: a dropped slot contributes nothing.
 //
 // One wave per token; each lane owns 16-byte column chunks.  Rows are gathered
-// (no atomics), summed in slot order in fp32 and rounded once, so the result is
-// deterministic.
+// (no atomics) and summed in slot order in fp32, then rounded once: the result is
+// deterministic.  The loads of all k slots (and the shared row) for a chunk are
+// issued before any arithmetic, so a wave keeps k + 1 loads in flight; k is a
+// template parameter for the common values.
 #include "common.h"
 #include "kernels.h"
 
@@ -15,12 +17,28 @@ namespace moe {
 namespace {
 
 template <bool BF16>
+__device__ __forceinline__ void accumulate(float* acc, const u32x4 v, float w) {
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] = fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);
+      acc[2 * q + 1] = fmaf(w, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, __uint_as_float(v[q]), acc[q]);
+  }
+}
+
+// KT > 0: k known at compile time; KT == 0: runtime k (any value).
+template <bool BF16, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm,
                                                        const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ topk_w,
-                                                       const void* __restrict__ shared_y, int T, int k, int d,
+                                                       const void* __restrict__ shared_y, int T, int k_rt, int d,
                                                        void* __restrict__ y) {
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+  const int k = KT > 0 ? KT : k_rt;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
@@ -28,39 +46,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int64_t rows = (int64_t)T * k;
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
   const char* yp = static_cast<const char*>(y_perm);
+  const char* sh = static_cast<const char*>(shared_y);
   for (int c = lane; c < chunks; c += 64) {
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = row_of[(size_t)t * k + j];
-      if (r < 0 || r >= rows) continue;
-      const float w = topk_w[(size_t)t * k + j];
-      const u32x4 v = ld16(yp + (size_t)r * row_bytes + (size_t)c * 16);
-      if (BF16) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if constexpr (KT > 0) {
+      u32x4 v[KT];
+      float w[KT];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(w, __uint_as_float(v[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(w, __uint_as_float(v[q] & 0xffff0000u), acc[2 * q + 1]);
-        }
-      } else {
+      for (int j = 0; j < KT; ++j) {
+        const int r = row_of[(size_t)t * KT + j];
+        const bool kept = r >= 0 && r < rows;
+        w[j] = kept ? topk_w[(size_t)t * KT + j] : 0.f;
+        v[j] = kept ? ld16(yp + (size_t)r * row_bytes + (size_t)c * 16) : zero;
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = fmaf(w, __uint_as_float(v[q]), acc[q]);
+      for (int j = 0; j < KT; ++j) accumulate<BF16>(acc, v[j], w[j]);
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int r = row_of[(size_t)t * k + j];
+        if (r < 0 || r >= rows) continue;
+        accumulate<BF16>(acc, ld16(yp + (size_t)r * row_bytes + (size_t)c * 16), topk_w[(size_t)t * k + j]);
       }
     }
-    if (shared_y != nullptr) {
-      const u32x4 v = ld16(static_cast<const char*>(shared_y) + (size_t)t * row_bytes + (size_t)c * 16);
-      if (BF16) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += __uint_as_float(v[q] << 16);
-          acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
-      }
-    }
+    if (sh != nullptr) accumulate<BF16>(acc, ld16(sh + (size_t)t * row_bytes + (size_t)c * 16), 1.f);
     u32x4 o;
     if (BF16) {
 #pragma unroll
@@ -74,17 +85,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   }
 }
 
+template <bool BF16>
+hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+#define MOE_COMBINE(KT)                                                                                 \
+  hipLaunchKernelGGL((combine_kernel<BF16, KT>), grid, block, 0, stream, a.y_perm, a.row_of, a.topk_w, \
+                     a.shared_y, a.T, a.k, a.d, a.y)
+  switch (a.k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 4: MOE_COMBINE(4); break;
+    case 8: MOE_COMBINE(8); break;
+    default: MOE_COMBINE(0); break;
+  }
+#undef MOE_COMBINE
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  const dim3 grid((a.T + 3) / 4), block(256);
-  if (a.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, a.y_perm, a.row_of, a.topk_w, a.shared_y,
-                       a.T, a.k, a.d, a.y);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, a.y_perm, a.row_of, a.topk_w,
-                       a.shared_y, a.T, a.k, a.d, a.y);
-  return hipGetLastError();
+  return a.dtype == MOE_BF16 ? launch_dtype<true>(a, stream) : launch_dtype<false>(a, stream);
 }
 
 }  // namespace moe

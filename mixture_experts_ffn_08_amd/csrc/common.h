@@ -82,3 +82,44 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// DPP lane permutations inside each row of 16 lanes (GFX9 encodings).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over each row of 16 lanes; every lane of the row gets the same value.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+// Inverse of order_key (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+}  // namespace moe

@@ -6,16 +6,32 @@
 //
 // C[r] = A[r] B_g^T for rows r of group g (dual: C = SiLU(A B0_g^T) * (A B1_g^T)).
 // A is [rows][K] and B is [N][K], both K-contiguous, so both MFMA operands load
-// as 16-byte K-vectors with no transpose.
+// as 16-byte K-vectors with no transpose.  With a row index, row r of A is read
+// from A[a_rows[r]]: the gate/up GEMM then gathers token rows straight from x
+// (the dispatch permutation) instead of reading a materialized copy.
 //
-// bf16 kernel: 256 threads (2 x 2 waves), block tile 128 rows x 128 columns (of
-// each B in the dual form), K step 64.  Global -> registers -> LDS with the next
-// K step prefetched into registers while the current one is multiplied; MFMA
-// 32x32x16 bf16 with fp32 accumulation; SiLU * up fused into the epilogue.
-// Tiles of all groups are enumerated on the device: each block scans the
-// per-group tile counts (from offsets) to find its group and first row, so the
-// host never reads the routing back.
+// bf16 kernel (gfx950):
+//  * 256 threads = 4 waves; block tile 256 rows x 256 B-rows (dual: 128 gate rows
+//    and the same 128 up rows, so one block produces 256 x 128 of SiLU*up);
+//    each wave owns 128 x 128 as 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators).
+//    A 256 x 256 tile is the smallest for which LDS reads + writes per K step stay
+//    under the MFMA time of the step with 4 waves.
+//  * K step 64; global -> registers -> LDS, two LDS stages (147 KB) and two
+//    register sets: the 16-byte loads of step kt+2 are issued while step kt is
+//    multiplied, because under full load a global round trip takes longer than one
+//    step of MFMA work.  One barrier per step, a plain s_barrier (a __syncthreads
+//    fence would also wait for the loads in flight).  LDS rows padded to 144 bytes:
+//    conflict-free ds_read_b128.  Within a step, the fragments of the next 16-wide
+//    k slice are read while the current one is multiplied.
+//  * MFMA operands swapped (weights as the "A" input), so each lane's accumulators
+//    hold 4 consecutive output columns: the epilogue packs them into 8-byte stores;
+//    SiLU(gate) * up is applied there in fp32.
+//  * Tiles of all groups are enumerated on the device from offsets (no host round
+//    trip); hardware block ids are remapped so that each XCD (blocks are dealt
+//    round-robin to the 8 XCDs) works on a contiguous run of tiles: the same expert's
+//    weights and the same rows stay in that XCD's L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -23,164 +39,240 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int LDS_STRIDE = BK + 8;             // bf16 elements per LDS row (16-byte pad)
+constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
+constexpr int kXcds = 8;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
 
-// Block-wide: locate m-tile `mt` among the groups.  Returns false (uniformly) when
-// mt is past the last tile.
-__device__ bool find_tile(const int32_t* __restrict__ offsets, int G, int max_rows, int mt, int& g,
-                          int& row0, int& row_end) {
-  __shared__ int s_incl[256];
-  __shared__ int s_wave_tot[4];
-  __shared__ int s_info[3];
+struct TileScan {
+  int incl[256];  // inclusive prefix of per-group m-tile counts
+  int wave_tot[4];
+};
+
+// Block-wide: per-group m-tile counts and their inclusive prefix; returns the total.
+__device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, TileScan& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int lo = 0, hi = 0, cnt = 0;
+  int cnt = 0;
   if (tid < G) {
-    lo = clamp_off(offsets[tid], max_rows);
-    hi = clamp_off(offsets[tid + 1], max_rows);
+    const int lo = clamp_off(offsets[tid], max_rows), hi = clamp_off(offsets[tid + 1], max_rows);
     cnt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
   }
-  // inclusive scan of cnt over the 256 threads
   int v = cnt;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int u = __shfl_up(v, o, 64);
     if (lane >= o) v += u;
   }
-  if (lane == 63) s_wave_tot[wave] = v;
-  if (tid == 0) s_info[0] = -1;
+  if (lane == 63) s.wave_tot[wave] = v;
   __syncthreads();
-  for (int w = 0; w < wave; ++w) v += s_wave_tot[w];
-  s_incl[tid] = v;
+  for (int w = 0; w < wave; ++w) v += s.wave_tot[w];
+  s.incl[tid] = v;
   __syncthreads();
-  const int total = s_incl[255];
-  if (mt >= total) return false;
-  const int excl = v - cnt;
-  if (tid < G && cnt > 0 && mt >= excl && mt < v) {
-    s_info[0] = tid;
-    s_info[1] = lo + (mt - excl) * BM;
-    s_info[2] = hi;
-  }
-  __syncthreads();
-  g = s_info[0];
-  row0 = s_info[1];
-  row_end = s_info[2];
-  return g >= 0;
+  return s.incl[255];
 }
 
-template <bool DUAL>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
-    int n_tiles) {
-  constexpr int NMAT = DUAL ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[NMAT][BN * LDS_STRIDE];
+// Group g holding m-tile mt (binary search on the inclusive prefix), its first row
+// and end row.
+__device__ void locate(const int32_t* __restrict__ offsets, int G, int max_rows, const TileScan& s, int mt,
+                       int& g, int& row0, int& row_end) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s.incl[mid] > mt) hi = mid; else lo = mid + 1;
+  }
+  g = lo;
+  const int excl = g > 0 ? s.incl[g - 1] : 0;
+  row0 = clamp_off(offsets[g], max_rows) + (mt - excl) * BM;
+  row_end = clamp_off(offsets[g + 1], max_rows);
+}
 
-  const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+// Logical tile of hardware block `bid` among `active` live blocks: XCD x = bid % 8
+// takes the x-th contiguous run of the live tiles.
+__device__ __forceinline__ int xcd_remap(int bid, int active) {
+  const int x = bid % kXcds, j = bid / kXcds;
+  const int per = active / kXcds, rem = active % kXcds;
+  return x * per + min(x, rem) + j;
+}
+
+// Block barrier without the memory fence of __syncthreads (which would also wait
+// for the global loads still in flight): LDS writes are drained first, and the
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool DUAL>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
+    const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ TileScan scan;
+
+  const int total = scan_tiles(offsets, G, max_rows, scan) * n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= total) return;
+  const int tile = xcd_remap(bid, total);
+  const int mt = tile / n_tiles, nt = tile % n_tiles;
   int g, row0, row_end;
-  if (!find_tile(offsets, G, max_rows, mt, g, row0, row_end)) return;
+  locate(offsets, G, max_rows, scan, mt, g, row0, row_end);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = nt * BN;
+  // B rows of this tile: dual -> gate rows [n0, n0+128) then up rows [n0, n0+128);
+  // single -> rows [n0, n0+256) (clamped at N; columns past N are not stored).
+  const int n0 = DUAL ? nt * (BN / 2) : nt * BN;
 
-  // Copy mapping: a 128 x 64 tile is 1024 16-byte chunks; thread tid moves chunks
-  // tid + 256*i: row (tid >> 3) + 32*i, column 8*(tid & 7).
+  // Copy mapping: each operand tile is 256 rows x 8 chunks of 16 bytes; thread tid
+  // moves chunks tid + 256 i: row (tid >> 3) + 32 i, k offset 8 (tid & 7).
+  // Addresses: block-uniform bases (scalar registers) plus 32-bit byte offsets per
+  // thread (the host checks that every operand fits in 4 GiB).
   const int crow = tid >> 3, ccol = 8 * (tid & 7);
-  const uint16_t* a_src[4];
-  const uint16_t* b_src[NMAT][4];
+  const char* a_base = reinterpret_cast<const char*>(A);
+  const char* b_base0 = reinterpret_cast<const char*>(B0 + (size_t)g * N * K);
+  const char* b_base1 = DUAL ? reinterpret_cast<const char*>(B1 + (size_t)g * N * K) : b_base0;
+  uint32_t a_off8[8], b_off8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int r = min(row0 + crow + 32 * i, row_end - 1);
+    if (a_rows != nullptr) r = min(max(a_rows[r], 0), a_nrows - 1);  // gather through the row index
+    a_off8[i] = ((uint32_t)r * (uint32_t)K + ccol) * 2u;
+    const int br = crow + 32 * i;
+    const int nrow = DUAL ? n0 + (br & (BN / 2 - 1)) : min(n0 + br, N - 1);
+    b_off8[i] = ((uint32_t)nrow * (uint32_t)K + ccol) * 2u;
+  }
+
+  // Two register sets: the loads of K step kt+2 are issued while step kt is
+  // multiplied and step kt+1 is still in flight.
+  u32x4 ra[2][8], rb[2][8];
+  auto load = [&](auto set, int k0) {
+    constexpr int S = decltype(set)::value;
+    const uint32_t kb = (uint32_t)k0 * 2u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[S][i] = ld16(a_base + (a_off8[i] + kb));
+      rb[S][i] = ld16((DUAL && i >= 4 ? b_base1 : b_base0) + (b_off8[i] + kb));
+    }
+  };
+  auto store = [&](auto set, int stage) {
+    constexpr int S = decltype(set)::value;
+    uint16_t* sa = lds + stage * STAGE;
+    uint16_t* sb = sa + BM * LDS_STRIDE;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      st16(sa + (crow + 32 * i) * LDS_STRIDE + ccol, ra[S][i]);
+      st16(sb + (crow + 32 * i) * LDS_STRIDE + ccol, rb[S][i]);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment offsets inside a stage: A rows wm*128 + 32 i; B rows per the layout above.
+  const int frow = lane & 31, half = lane >> 5, fk = 8 * half;
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_off[i] = (wm * 128 + i * 32 + frow) * LDS_STRIDE + fk;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // dual: fragments 0,1 = gate rows wn*64 + {0,32}; 2,3 = the same rows of up
+    const int brow = DUAL ? (j >> 1) * (BN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+    b_off[j] = (BM + brow + frow) * LDS_STRIDE + fk;
+  }
+  bf16x8 fa[2][4], fb[2][4];
+  auto read_frags = [&](const uint16_t* st, int ks, int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[buf][i] = as_bf16x8(ld16(st + a_off[i] + ks));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[buf][j] = as_bf16x8(ld16(st + b_off[j] + ks));
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fb[buf][j], fa[buf][i], acc[i][j]);
+  };
+
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  const int nk = K / BK;  // even: K % 128 == 0
+  load(R0{}, 0);
+  load(R1{}, min(BK, (nk - 1) * BK));
+  store(R0{}, 0);
+  lds_barrier();
+  read_frags(lds, 0, 0);
+  // Step kt: stage kt & 1 is in LDS, register set kt & 1 is free again, set
+  // (kt + 1) & 1 holds step kt+1 in flight.  The step has no branches (a join
+  // would make the compiler's wait counts drain the set just issued): past the end
+  // it re-loads the last K chunk, and what that writes to LDS is never read.
+  const int last = (nk - 1) * BK;
+  auto step = [&](auto set, int kt) {
+    constexpr int S = decltype(set)::value;
+    using Other = std::integral_constant<int, S ^ 1>;
+    load(set, min((kt + 2) * BK, last));
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
+    const uint16_t* st = lds + S * STAGE;
+    read_frags(st, 16, 1);
+    mma(0);
+    read_frags(st, 32, 0);
+    mma(1);
+    read_frags(st, 48, 1);
+    mma(0);
+    mma(1);
+    store(Other{}, S ^ 1);
+    // Order: the 8 fragment reads of k slice s+1, then the 16 MFMAs of slice s.
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);    // DS writes of the next stage
+    lds_barrier();
+    read_frags(lds + (S ^ 1) * STAGE, 0, 0);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(R0{}, kt);
+    step(R1{}, kt + 1);
+  }
+
+  // Epilogue.  acc[i][j] element r of lane l: output row (m) = 32 i + l % 32 of the
+  // wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of fragment j;
+  // each lane writes 4 consecutive columns (8 bytes).  (Staging the tile through LDS
+  // for full-row writes measured slower.)
+  const int m_base = row0 + wm * 128 + frow;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = min(row0 + crow + 32 * i, row_end - 1);
-    a_src[i] = A + (size_t)r * K + ccol;
-    const size_t brow = (size_t)g * N + n0 + crow + 32 * i;
-    b_src[0][i] = B0 + brow * K + ccol;
-    if (DUAL) b_src[NMAT - 1][i] = B1 + brow * K + ccol;
-  }
-
-  u32x4 ra[4], rb[NMAT][4];
+    const int row = m_base + i * 32;
+    if (row >= row_end) continue;
+    uint16_t* crow_ptr = C + (size_t)row * N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = ld16(a_src[i]);
+    for (int j = 0; j < (DUAL ? 2 : 4); ++j)
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) rb[m][i] = ld16(b_src[m][i]);
-  }
-
-  f32x16 acc[NMAT][2][2];
+      for (int q = 0; q < 4; ++q) {
+        const int col = (DUAL ? n0 + wn * 64 : n0 + wn * 128) + j * 32 + 8 * q + 4 * half;
+        if (!DUAL && col >= N) continue;
+        float v[4];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.f;
-
-  const int frow = lane & 31, fk = 8 * (lane >> 5);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      st16(&sA[(crow + 32 * i) * LDS_STRIDE + ccol], ra[i]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m) st16(&sB[m][(crow + 32 * i) * LDS_STRIDE + ccol], rb[m][i]);
-    }
-    __syncthreads();
-    if (k0 + BK < K) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = ld16(a_src[i] + k0 + BK);
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) rb[m][i] = ld16(b_src[m][i] + k0 + BK);
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8 af[2], bfr[NMAT][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = as_bf16x8(ld16(&sA[(wm * 64 + i * 32 + frow) * LDS_STRIDE + ks + fk]));
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[m][j] = as_bf16x8(ld16(&sB[m][(wn * 64 + j * 32 + frow) * LDS_STRIDE + ks + fk]));
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[m][i][j] = mfma32x32x16(af[i], bfr[m][j], acc[m][i][j]);
-    }
-  }
-
-  // Epilogue: accumulator element r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32 of its 32 x 32 fragment.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < row_end) {
-          float v = acc[0][i][j][r];
-          if (DUAL) {
-            const float u = acc[NMAT - 1][i][j][r];
-            v = v / (1.f + expf(-v)) * u;
-          }
-          C[(size_t)row * N + col] = f32_to_bf16(v);
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[i][j][4 * q + e];
+          v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + 2][4 * q + e] : x;
         }
+        const uint32_t p0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t p1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(crow_ptr + col) = make_uint2(p0, p1);
       }
-    }
+  }
 }
 
 // fp32 path: one thread per output element, plain K loop.
 template <bool DUAL>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __restrict__ A,
+                                                                const int32_t* __restrict__ a_rows, int a_nrows,
                                                                 const int32_t* __restrict__ offsets, int G,
                                                                 int max_rows, int N, int K,
                                                                 const float* __restrict__ B0,
@@ -195,7 +287,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
     if (row >= lo && row < hi) { g = q; break; }
   }
   if (g < 0) return;
-  const float* a = A + (size_t)row * K;
+  const int ar = a_rows != nullptr ? min(max(a_rows[row], 0), a_nrows - 1) : row;
+  const float* a = A + (size_t)ar * K;
   const float* b0 = B0 + ((size_t)g * N + n) * K;
   float s0 = 0.f, s1 = 0.f;
   if (DUAL) {
@@ -215,29 +308,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
   if (a.dtype == MOE_BF16) {
-    const int n_tiles = a.N / BN;
+    const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
     const int64_t m_tiles = (a.max_rows + BM - 1) / BM + std::min(a.G, a.max_rows);
     const int64_t blocks = m_tiles * n_tiles;
     if (blocks <= 0) return hipSuccess;
     if (dual)
       hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,
-                         (const uint16_t*)a.B1, (uint16_t*)a.C, n_tiles);
+                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const uint16_t*)a.B0, (const uint16_t*)a.B1, (uint16_t*)a.C, n_tiles);
     else
       hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,
-                         nullptr, (uint16_t*)a.C, n_tiles);
+                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const uint16_t*)a.B0, nullptr, (uint16_t*)a.C, n_tiles);
   } else {
     const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;
     if (blocks <= 0) return hipSuccess;
     if (dual)
       hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const float*)a.A, a.offsets, a.G, a.max_rows, a.N, a.K, (const float*)a.B0,
-                         (const float*)a.B1, (float*)a.C);
+                         (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const float*)a.B0, (const float*)a.B1, (float*)a.C);
     else
       hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const float*)a.A, a.offsets, a.G, a.max_rows, a.N, a.K, (const float*)a.B0,
-                         nullptr, (float*)a.C);
+                         (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const float*)a.B0, nullptr, (float*)a.C);
   }
   return hipGetLastError();
 }

@@ -44,7 +44,9 @@ struct PermuteArgs {
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
 struct GroupedGemmArgs {
-  const void* A;        // [max_rows][K]
+  const void* A;        // [max_rows][K], or [a_nrows][K] read through a_rows
+  const int32_t* a_rows;  // null, or row r of the product reads A[a_rows[r]]
+  int a_nrows;
   const int32_t* offsets;
   int G, max_rows, N, K;
   const void* B0;       // [G][N][K]

@@ -155,6 +155,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
                      a.capacity, a.block_base, a.counts, a.offsets);
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
                      a.block_base, a.offsets, a.row_of, a.perm_token);
+  if (a.x_perm == nullptr) return hipGetLastError();
   const int max_rows = (int)P;
   const int blocks = (int)std::min<int64_t>((max_rows + 3) / 4, 8192);
   hipLaunchKernelGGL(gather_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,

@@ -7,11 +7,16 @@
 // them.  Transformers & Math 17.2: the two softmax orders.
 //
 // One block of 4 waves takes 64 tokens and every expert (E <= 256, padded to
-// EP = 16*NB).  bf16: the score tile is a 64 x EP MFMA GEMM (16x16x32 bf16, fp32
-// accumulate); router weight chunks of 64 k-values are staged in LDS and shared
-// by the 4 waves, x rows stream straight from HBM into MFMA operands.  The fp32
-// tile goes to LDS, then each wave selects top-k for its 16 tokens with
-// ds_swizzle butterflies and writes scores, indices, weights and near-tie flags.
+// EP = 16*NB).
+//  * Scores (bf16): a 64 x EP MFMA GEMM (16x16x32 bf16, fp32 accumulate).  Each
+//    wave owns 16 tokens; router-weight chunks of 256 k-values (128 for E > 128)
+//    are staged in a double-buffered LDS ring shared by the 4 waves, and the next
+//    chunk (and the next x operands) are fetched into registers while the current
+//    one is multiplied.  fp32 inputs take a plain FMA loop.
+//  * Selection: the fp32 score tile goes to LDS; each 16-lane row of a wave takes
+//    one token (4 tokens per wave at once), lane r holding experts r + 16 i.
+//    k+1 rounds of arg-max over (score, -index) with DPP butterflies inside the
+//    row; the owner lane retires each winner.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,15 +24,23 @@ namespace moe {
 namespace {
 
 constexpr int kTokens = 64;   // tokens per block
-constexpr int kWsStride = 72; // bf16 elements per staged router row: 64 + 8 pad
 
+// K chunk per pipeline stage: large enough that each stage keeps many bytes in
+// flight (a stage round trip is latency-bound), small enough for two stages of
+// router weights in LDS.
 template <int NB>
 struct RouteLds {
   static constexpr int EP = NB * 16;
-  static constexpr int kTileStride = EP + 4;  // floats; breaks 4-row bank aliasing
+  static constexpr int BK = EP <= 128 ? 256 : 128;
+  static constexpr int kWsStride = BK + 8;               // bf16 per staged router row (16-byte pad)
+  static constexpr int kTileStride = EP + 4;             // floats; breaks 4-row bank aliasing
   static constexpr int kTileBytes = kTokens * kTileStride * 4;
-  static constexpr int kWsBytes = EP * kWsStride * 2;
+  static constexpr int kWsBytes = 2 * EP * kWsStride * 2;  // two stages
   static constexpr int kBytes = kTileBytes > kWsBytes ? kTileBytes : kWsBytes;
+  static constexpr int kRowChunks = BK / 8;              // 16-byte chunks per router row per stage
+  static constexpr int kChunks = EP * kRowChunks;
+  static constexpr int kChunksPerThread = (kChunks + 255) / 256;
+  static constexpr int kSteps = BK / 32;                 // MFMA k-steps per stage
 };
 
 // a beats b: larger key, or equal key and lower expert index.
@@ -35,92 +48,89 @@ __device__ __forceinline__ bool beats(uint32_t ao, uint32_t ai, uint32_t bo, uin
   return ao > bo || (ao == bo && ai < bi);
 }
 
-template <int X>
+template <int CTRL>
 __device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi) {
-  uint32_t oo = swz_xor<X>(bo), oi = swz_xor<X>(bi);
+  const uint32_t oo = dpp<CTRL>(bo), oi = dpp<CTRL>(bi);
   if (beats(oo, oi, bo, bi)) { bo = oo; bi = oi; }
 }
 
-// Top-k for rows [lr0, lr0 + nrows) of the score tile; executed by one wave.
-__device__ void select_rows(const float* tile, int stride, int t0, int lr0, int nrows, int T, int E,
-                            int k, int mode, int renorm, float* __restrict__ logits,
-                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                            int32_t* __restrict__ near_tie) {
-  const int lane = threadIdx.x & 63;
-  for (int lr = lr0; lr < lr0 + nrows; ++lr) {
+// Top-k for the 64 tokens of a score tile.  Wave w takes tokens 16w .. 16w+15,
+// four at a time (one per 16-lane row).  NB keys per lane; SPL result slots per
+// lane (slot j lives in lane j % 16, register j / 16).
+template <int NB, int SPL>
+__device__ void select_tile(const float* tile, int stride, int t0, int T, int E, int k, int mode, int renorm,
+                            float* __restrict__ logits, int32_t* __restrict__ topk_idx,
+                            float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, row = lane >> 4;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int lr = wave * 16 + pass * 4 + row;
     const int t = t0 + lr;
-    if (t >= T) break;
+    const bool live = t < T;
     const float* s = tile + lr * stride;
-    float kf[4];
-    uint32_t ko[4];
+    float kf[NB];
+    uint32_t ko[NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
+    for (int i = 0; i < NB; ++i) {
+      const int e = r + 16 * i;
       const bool present = e < E;
       const float v = present ? s[e] : 0.f;
       kf[i] = v;
       ko[i] = present ? max(order_key(v), 1u) : 0u;  // 0 marks "absent or taken"
-      if (present) logits[(size_t)t * E + e] = v;
+      if (present && live) logits[(size_t)t * E + e] = v;
     }
     const int rounds = k < E ? k + 1 : k;
-    uint32_t my_idx[4] = {0, 0, 0, 0};
-    float my_key[4] = {0.f, 0.f, 0.f, 0.f};
-    float top = 0.f, kth = 0.f, next = 0.f;
-    for (int r = 0; r < rounds; ++r) {
+    uint32_t my_idx[SPL];
+    float my_key[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) { my_idx[q] = 0u; my_key[q] = 0.f; }
+    float top = 0.f, kth = 0.f, next = 0.f, ssum = 0.f;
+    for (int j = 0; j < rounds; ++j) {
       uint32_t bo = 0u, bi = 0xffffffffu;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (ko[i] > bo) { bo = ko[i]; bi = lane + 64 * i; }  // strict: lower index keeps ties
-      argmax_step<1>(bo, bi);
-      argmax_step<2>(bo, bi);
-      argmax_step<4>(bo, bi);
-      argmax_step<8>(bo, bi);
-      argmax_step<16>(bo, bi);
-      const uint32_t o0 = __builtin_amdgcn_readlane(bo, 0), i0 = __builtin_amdgcn_readlane(bi, 0);
-      const uint32_t o1 = __builtin_amdgcn_readlane(bo, 32), i1 = __builtin_amdgcn_readlane(bi, 32);
-      const uint32_t wi = beats(o1, i1, o0, i0) ? i1 : i0;
-      const float wkey = s[wi];
-      if (r == 0) top = wkey;
-      if (r < k) {
-        if (r == k - 1) kth = wkey;
+      for (int i = 0; i < NB; ++i)
+        if (ko[i] > bo) { bo = ko[i]; bi = r + 16 * i; }  // strict: the lower index keeps a tie
+      argmax_step<kDppXor1>(bo, bi);
+      argmax_step<kDppXor2>(bo, bi);
+      argmax_step<kDppHalfMirror>(bo, bi);
+      argmax_step<kDppMirror>(bo, bi);
+      const float wkey = key_value(bo);
+      if (j == 0) top = wkey;
+      if (j < k) {
+        if (j == k - 1) kth = wkey;
+        ssum += expf(wkey - top);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (r == lane + 64 * q) { my_idx[q] = wi; my_key[q] = wkey; }
+        for (int q = 0; q < SPL; ++q)
+          if (j == r + 16 * q) { my_idx[q] = bi; my_key[q] = wkey; }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (wi == (uint32_t)(lane + 64 * i)) ko[i] = 0u;
+        for (int i = 0; i < NB; ++i)
+          if (bi == (uint32_t)(r + 16 * i)) ko[i] = 0u;
       } else {
         next = wkey;
       }
     }
-    // Softmax pieces, relative to the best score.
     float z = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) z += expf(kf[i] - top);
-    float ej[4], esum = 0.f;
+    for (int i = 0; i < NB; ++i)
+      if (r + 16 * i < E) z += expf(kf[i] - top);
+    z = row16_sum(z);
+    const float denom = (mode == MOE_TOPK_THEN_SOFTMAX || renorm) ? ssum : z;
+    if (live) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ej[q] = (lane + 64 * q < k) ? expf(my_key[q] - top) : 0.f;
-      esum += ej[q];
-    }
-    const float Z = wave_sum(z);
-    const float S = wave_sum(esum);
-    const float denom = (mode == MOE_TOPK_THEN_SOFTMAX || renorm) ? S : Z;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = lane + 64 * q;
-      if (j < k) {
-        topk_idx[(size_t)t * k + j] = (int32_t)my_idx[q];
-        topk_w[(size_t)t * k + j] = ej[q] / denom;
+      for (int q = 0; q < SPL; ++q) {
+        const int j = r + 16 * q;
+        if (j < k) {
+          topk_idx[(size_t)t * k + j] = (int32_t)my_idx[q];
+          topk_w[(size_t)t * k + j] = expf(my_key[q] - top) / denom;
+        }
       }
+      if (r == 0) near_tie[t] = (k < E && ((double)kth - (double)next) < MOE_NEAR_TIE_GAP) ? 1 : 0;
     }
-    if (lane == 0)
-      near_tie[t] = (k < E && ((double)kth - (double)next) < MOE_NEAR_TIE_GAP) ? 1 : 0;
   }
 }
 
-template <int NB>
+template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int k, int mode, int renorm, float* __restrict__ logits,
@@ -135,32 +145,67 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   const int kg = lane >> 4;
   const int arow = min(t0 + wave * 16 + (lane & 15), T - 1);
   const uint16_t* xrow = x + (size_t)arow * d;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // Router-weight chunk c of a stage: row n = c / kRowChunks, k offset 8 * (c % kRowChunks).
+  u32x4 wreg[L::kChunksPerThread];
+  auto load_w = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < L::kChunksPerThread; ++i) {
+      const int c = tid + 256 * i;
+      const int n = c / L::kRowChunks, kc = k0 + 8 * (c % L::kRowChunks);
+      wreg[i] = (c < L::kChunks && n < E && kc < d) ? ld16(wr + (size_t)n * d + kc) : zero;
+    }
+  };
+  auto store_w = [&](int stage) {
+    uint16_t* dst = ws + stage * (L::EP * L::kWsStride);
+#pragma unroll
+    for (int i = 0; i < L::kChunksPerThread; ++i) {
+      const int c = tid + 256 * i;
+      if (c < L::kChunks) st16(dst + (c / L::kRowChunks) * L::kWsStride + 8 * (c % L::kRowChunks), wreg[i]);
+    }
+  };
+  // x operand of k-step s of the stage: 8 values at k0 + 32 s + 8 kg of this lane's token.
+  u32x4 areg[L::kSteps], anext[L::kSteps];
+  auto load_a = [&](int k0, u32x4* dst) {
+#pragma unroll
+    for (int s = 0; s < L::kSteps; ++s) {
+      const int ka = k0 + 32 * s + 8 * kg;
+      dst[s] = ka < d ? ld16(xrow + ka) : zero;
+    }
+  };
 
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < d; k0 += 64) {
-    const int ka = k0 + 8 * kg, kb = k0 + 32 + 8 * kg;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const u32x4 a0 = ka < d ? ld16(xrow + ka) : zero;
-    const u32x4 a1 = kb < d ? ld16(xrow + kb) : zero;
-    __syncthreads();
-    for (int c = tid; c < L::EP * 8; c += 256) {
-      const int n = c >> 3, kc = k0 + 8 * (c & 7);
-      u32x4 v = zero;
-      if (n < E && kc < d) v = ld16(wr + (size_t)n * d + kc);
-      st16(ws + n * kWsStride + 8 * (c & 7), v);
+  load_a(0, areg);
+  load_w(0);
+  store_w(0);
+  __syncthreads();
+  int stage = 0;
+  for (int k0 = 0; k0 < d; k0 += L::BK) {
+    const bool more = k0 + L::BK < d;
+    if (more) {
+      load_a(k0 + L::BK, anext);
+      load_w(k0 + L::BK);
     }
-    __syncthreads();
+    const uint16_t* cur = ws + stage * (L::EP * L::kWsStride);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint16_t* brow = ws + (nb * 16 + (lane & 15)) * kWsStride + 8 * kg;
-      acc[nb] = mfma16x16x32(as_bf16x8(a0), as_bf16x8(ld16(brow)), acc[nb]);
-      acc[nb] = mfma16x16x32(as_bf16x8(a1), as_bf16x8(ld16(brow + 32)), acc[nb]);
+      const uint16_t* brow = cur + (nb * 16 + (lane & 15)) * L::kWsStride + 8 * kg;
+#pragma unroll
+      for (int s = 0; s < L::kSteps; ++s)
+        acc[nb] = mfma16x16x32(as_bf16x8(areg[s]), as_bf16x8(ld16(brow + 32 * s)), acc[nb]);
     }
+    if (more) {
+      store_w(stage ^ 1);
+#pragma unroll
+      for (int s = 0; s < L::kSteps; ++s) areg[s] = anext[s];
+    }
+    __syncthreads();
+    stage ^= 1;
   }
-  __syncthreads();
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int n = nb * 16 + (lane & 15);
@@ -169,11 +214,10 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     for (int i = 0; i < 4; ++i) tile[(wave * 16 + 4 * kg + i) * L::kTileStride + n] = acc[nb][i] + b;
   }
   __syncthreads();
-  select_rows(tile, L::kTileStride, t0, wave * 16, 16, T, E, k, mode, renorm, logits, topk_idx, topk_w,
-              near_tie);
+  select_tile<NB, SPL>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie);
 }
 
-template <int NB>
+template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, int T,
     int d, int E, int k, int mode, int renorm, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
@@ -195,23 +239,28 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     tile[lr * L::kTileStride + n] = acc;
   }
   __syncthreads();
-  const int wave = tid >> 6;
-  select_rows(tile, L::kTileStride, t0, wave * 16, 16, T, E, k, mode, renorm, logits, topk_idx, topk_w,
-              near_tie);
+  select_tile<NB, SPL>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie);
+}
+
+template <int NB, int SPL>
+hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
+  const dim3 grid((a.T + kTokens - 1) / kTokens), block(256);
+  if (a.dtype == MOE_BF16)
+    hipLaunchKernelGGL((route_bf16_kernel<NB, SPL>), grid, block, 0, stream, (const uint16_t*)a.x,
+                       (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
+                       a.topk_idx, a.topk_w, a.near_tie);
+  else
+    hipLaunchKernelGGL((route_f32_kernel<NB, SPL>), grid, block, 0, stream, (const float*)a.x,
+                       (const float*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
+                       a.topk_idx, a.topk_w, a.near_tie);
+  return hipGetLastError();
 }
 
 template <int NB>
 hipError_t launch_nb(const RouteArgs& a, hipStream_t stream) {
-  const dim3 grid((a.T + kTokens - 1) / kTokens), block(256);
-  if (a.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_bf16_kernel<NB>, grid, block, 0, stream, (const uint16_t*)a.x,
-                       (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
-                       a.logits, a.topk_idx, a.topk_w, a.near_tie);
-  else
-    hipLaunchKernelGGL(route_f32_kernel<NB>, grid, block, 0, stream, (const float*)a.x,
-                       (const float*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
-                       a.topk_idx, a.topk_w, a.near_tie);
-  return hipGetLastError();
+  // slots per lane: one when k <= 16, else NB (k <= E <= 16 NB)
+  if (a.k <= 16) return launch_variant<NB, 1>(a, stream);
+  return launch_variant<NB, NB>(a, stream);
 }
 
 }  // namespace

@@ -5,9 +5,8 @@
 // Latent "Keeping the load balanced"; Understanding Data "Load imbalance"
 // (measured on demand, before any capacity cut).
 //
-// stats_partial_kernel: 64 tokens per block, one wave per token at a time,
-// softmax over all E (lane holds experts lane + 64 i), per-lane fp32 sums, then
-// the four waves' sums added in fixed order -> partial[block][E].
+// stats_partial_kernel: 64 tokens per block; per-token softmax normalizers, then
+// per-expert sums over the block's tokens in token order -> partial[block][E].
 // stats_final_kernel: one block; sums the partials in block order (fp64), then
 // f, P, L_aux and max/mean.  No atomics: results are deterministic.
 #include "common.h"
@@ -16,42 +15,42 @@
 namespace moe {
 namespace {
 
+// One block per 64 tokens.  The block's 64 x E score tile is copied to LDS with
+// all loads in flight; each 16-lane row of a wave then takes one token (max and
+// sum of exponentials with DPP butterflies), and finally thread e sums
+// exp(s[t][e] - max_t) / sum_t over the 64 tokens in token order.
 __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits, int T, int E,
                                                              float* __restrict__ partial) {
-  __shared__ float s_part[4][MOE_MAX_EXPERTS];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float tile[kStatsTokens * (MOE_MAX_EXPERTS + 1)];
+  __shared__ float s_max[kStatsTokens], s_inv[kStatsTokens];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kStatsTokens;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int lt = wave; lt < kStatsTokens; lt += 4) {
-    const int t = t0 + lt;
-    if (t >= T) break;
-    const float* s = logits + (size_t)t * E;
-    float v[4];
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = e < E ? s[e] : -INFINITY;
-      m = fmaxf(m, v[i]);
-    }
-    m = wave_max(m);
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (lane + 64 * i < E) ? expf(v[i] - m) : 0.f;
-      z += v[i];
-    }
-    z = wave_sum(z);
-    const float inv = 1.f / z;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += v[i] * inv;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (lane + 64 * i < E) s_part[wave][lane + 64 * i] = acc[i];
+  const int nt = min(kStatsTokens, T - t0);
+  const int stride = E + 1;
+  const float* src = logits + (size_t)t0 * E;
+  for (int i = tid; i < nt * E; i += 256) tile[(i / E) * stride + i % E] = src[i];
   __syncthreads();
-  for (int e = tid; e < E; e += 256)
-    partial[(size_t)blockIdx.x * E + e] = ((s_part[0][e] + s_part[1][e]) + s_part[2][e]) + s_part[3][e];
+  const int r = lane & 15;
+  for (int lt = wave * 4 + (lane >> 4); lt < kStatsTokens; lt += 16) {  // 16 tokens per pass
+    float m = -INFINITY;
+    if (lt < nt)
+      for (int e = r; e < E; e += 16) m = fmaxf(m, tile[lt * stride + e]);
+    m = row16_max(m);
+    float z = 0.f;
+    if (lt < nt)
+      for (int e = r; e < E; e += 16) z += expf(tile[lt * stride + e] - m);
+    z = row16_sum(z);
+    if (r == 0 && lt < nt) {
+      s_max[lt] = m;
+      s_inv[lt] = 1.f / z;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    float acc = 0.f;
+    for (int lt = 0; lt < nt; ++lt) acc += expf(tile[lt * stride + e] - s_max[lt]) * s_inv[lt];
+    partial[(size_t)blockIdx.x * E + e] = acc;
+  }
 }
 
 __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restrict__ counts,

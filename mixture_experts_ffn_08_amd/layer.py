@@ -57,9 +57,11 @@ class DeviceWeights:
 
 
 class Buffers:
-    """Every intermediate and output of the layer for T tokens (device memory)."""
+    """Every intermediate and output of the layer for T tokens (device memory).
+    x_perm (the gathered copy of x) is only allocated with ``gathered=True``;
+    by default the gate/up GEMM reads x through perm_token."""
 
-    def __init__(self, shape: LayerShape, T: int, device="cuda"):
+    def __init__(self, shape: LayerShape, T: int, device="cuda", gathered: bool = False):
         s = shape
         dev = torch.device(device)
         td = torch_dtype(s.dtype)
@@ -74,7 +76,7 @@ class Buffers:
         self.offsets = torch.empty((s.E + 1,), dtype=i32, device=dev)
         self.row_of = torch.empty((T, s.k), dtype=i32, device=dev)
         self.perm_token = torch.empty((max(R, 1),), dtype=i32, device=dev)
-        self.x_perm = torch.empty((max(R, 1), s.d), dtype=td, device=dev)
+        self.x_perm = torch.empty((max(R, 1), s.d), dtype=td, device=dev) if gathered else None
         self.a = torch.empty((max(R, 1), s.F), dtype=td, device=dev)
         self.y_perm = torch.empty((max(R, 1), s.d), dtype=td, device=dev)
         self.y = torch.empty((T, s.d), dtype=td, device=dev)
@@ -101,8 +103,8 @@ class MoeLayer:
         self.w = weights
         self.shape = weights.shape
 
-    def buffers(self, T: int) -> Buffers:
-        return Buffers(self.shape, T, self.w.device)
+    def buffers(self, T: int, gathered: bool = False) -> Buffers:
+        return Buffers(self.shape, T, self.w.device, gathered)
 
     def route(self, x, b: Buffers, stream=None):
         s = self.shape
@@ -110,24 +112,37 @@ class MoeLayer:
                        b.topk_idx, b.topk_w, b.near_tie, stream)
 
     def permute(self, x, b: Buffers, stream=None):
+        """Dispatch; also gathers x_perm when the buffers hold one."""
         s = self.shape
         cap = _lib.moe_capacity(b.T, s.k, s.E, s.phi)
         _lib.moe_permute(b.topk_idx, b.T, s.k, s.E, cap, x, s.d, b.counts, b.offsets, b.row_of, b.perm_token,
                          b.x_perm, b.ws_permute, stream)
 
-    def experts(self, b: Buffers, stream=None):
+    def gate_up(self, x, b: Buffers, stream=None):
         s = self.shape
         R = b.T * s.k
-        _lib.moe_grouped_gate_up(b.x_perm, b.offsets, s.E, R, s.d, s.F, self.w.gate, self.w.up, b.a, stream)
-        _lib.moe_grouped_down(b.a, b.offsets, s.E, R, s.F, s.d, self.w.down, b.y_perm, stream)
+        if b.x_perm is not None:
+            _lib.moe_grouped_gate_up(b.x_perm, None, 0, b.offsets, s.E, R, s.d, s.F, self.w.gate, self.w.up, b.a,
+                                     stream)
+        else:
+            _lib.moe_grouped_gate_up(x, b.perm_token, b.T, b.offsets, s.E, R, s.d, s.F, self.w.gate, self.w.up,
+                                     b.a, stream)
+
+    def down(self, b: Buffers, stream=None):
+        s = self.shape
+        _lib.moe_grouped_down(b.a, b.offsets, s.E, b.T * s.k, s.F, s.d, self.w.down, b.y_perm, stream)
+
+    def experts(self, x, b: Buffers, stream=None):
+        self.gate_up(x, b, stream)
+        self.down(b, stream)
 
     def shared_expert(self, x, b: Buffers, stream=None):
         s = self.shape
         if self.w.shared is None:
             return
         g, u, dn = self.w.shared
-        _lib.moe_grouped_swiglu(x, b.shared_offsets, 1, b.T, s.d, s.F_shared, g, u, dn, b.shared_a, b.shared_y,
-                                stream)
+        _lib.moe_grouped_swiglu(x, None, 0, b.shared_offsets, 1, b.T, s.d, s.F_shared, g, u, dn, b.shared_a,
+                                b.shared_y, stream)
 
     def combine(self, b: Buffers, stream=None):
         s = self.shape
@@ -147,7 +162,7 @@ class MoeLayer:
             return b
         self.route(x, b, stream)
         self.permute(x, b, stream)
-        self.experts(b, stream)
+        self.experts(x, b, stream)
         self.shared_expert(x, b, stream)
         self.combine(b, stream)
         self.stats(b, stream)

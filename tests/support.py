@@ -50,14 +50,14 @@ class ExpertCache:
 class GpuRun:
     """Upload one layer, run it once through the C ABI, keep host copies."""
 
-    def __init__(self, inp: minp.LayerInputs, device="cuda"):
+    def __init__(self, inp: minp.LayerInputs, device="cuda", gathered: bool = False):
         self.inp, self.shape = inp, inp.shape
         s = self.shape
         t0 = time.time()
         self.weights = DeviceWeights(inp, device)
         self.layer = MoeLayer(self.weights)
         self.x = to_device(inp.x, s.dtype, device)
-        self.bufs = Buffers(s, s.T, device)
+        self.bufs = Buffers(s, s.T, device, gathered)
         log(f"[{s.name}] uploaded T={s.T} d={s.d} E={s.E} k={s.k} F={s.F} Fs={s.F_shared} in {time.time() - t0:.1f}s")
 
     def run(self):

@@ -99,7 +99,7 @@ def permute(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(T=-3), -1), (dict(dtype=3), -1), (dict(k=9), -1), (dict(d=4), -2), (dict(idx=None), -1),
-    (dict(x_perm=None), -1), (dict(ws=None), -3), (dict(ws_bytes=8), -3), (dict(counts=None), -1),
+    (dict(x=None), -1), (dict(ws=None), -3), (dict(ws_bytes=8), -3), (dict(counts=None), -1),
 ])
 def test_permute_rejects_before_launch(kw, status):
     assert permute(**kw) == status
@@ -110,15 +110,16 @@ def test_permute_zero_tokens_is_a_no_op():
 
 
 def gate_up(**kw):
-    a = dict(xp=FAKE, off=FAKE, G=8, rows=16, d=256, F=384, wg=FAKE, wu=FAKE, dtype=1, out=FAKE)
+    a = dict(xp=FAKE, ri=None, src=0, off=FAKE, G=8, rows=16, d=256, F=384, wg=FAKE, wu=FAKE, dtype=1, out=FAKE)
     a.update(kw)
-    return _lib.load().moe_grouped_gate_up(a["xp"], a["off"], a["G"], a["rows"], a["d"], a["F"], a["wg"],
-                                           a["wu"], a["dtype"], a["out"], None)
+    return _lib.load().moe_grouped_gate_up(a["xp"], a["ri"], a["src"], a["off"], a["G"], a["rows"], a["d"], a["F"],
+                                           a["wg"], a["wu"], a["dtype"], a["out"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(G=0), -1), (dict(G=300), -2), (dict(rows=-1), -1), (dict(d=200), -2), (dict(F=136), -2),
     (dict(dtype=0, d=12), -2), (dict(dtype=9), -1), (dict(wg=None), -1), (dict(out=None), -1),
+    (dict(ri=FAKE, src=0), -1), (dict(xp=None), -1),
 ])
 def test_grouped_rejects_before_launch(kw, status):
     assert gate_up(**kw) == status
@@ -127,7 +128,7 @@ def test_grouped_rejects_before_launch(kw, status):
 def test_grouped_zero_rows_is_a_no_op():
     assert gate_up(rows=0, xp=None, off=None, wg=None, wu=None, out=None) == 0
     lib = _lib.load()
-    assert lib.moe_grouped_swiglu(None, None, 4, 0, 256, 256, None, None, None, 1, None, None, None) == 0
+    assert lib.moe_grouped_swiglu(None, None, 0, None, 4, 0, 256, 256, None, None, None, 1, None, None, None) == 0
     assert lib.moe_grouped_down(None, FAKE, 4, 8, 256, 256, FAKE, 1, FAKE, None) == -1
 
 

@@ -56,12 +56,11 @@ def test_config_parity(name):
         xs = minp.as_f32(inp.x, shape.dtype)
         ex = ExpertCache(inp)
         tol = TOL[shape.dtype]
-        # permuted rows: gather exact, gate/up and down within tolerance
+        # permuted rows: gate/up and down within tolerance
         rows = sample_rows(offsets, rng)
-        x_perm = host(b.x_perm[[r for _, r in rows]])
+        x_perm = xs[perm_token[[r for _, r in rows]]]      # the rows the gate/up GEMM gathers
         a_gpu = host(b.a[[r for _, r in rows]])
         y_gpu = host(b.y_perm[[r for _, r in rows]])
-        assert np.array_equal(x_perm, xs[perm_token[[r for _, r in rows]]])
         a_err = y_err = 0.0
         for i, (e, r) in enumerate(rows):
             g, u, dn = ex(e)

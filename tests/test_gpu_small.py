@@ -45,8 +45,9 @@ def full_check(inp, out):
     # experts on the GPU's own permuted rows
     R = int(offsets[-1])
     b = run_state["bufs"]
-    x_perm = host(b.x_perm)[:R]
-    assert np.array_equal(x_perm, xs[perm_token]), "x_perm must be an exact gather"
+    if b.x_perm is not None:
+        assert np.array_equal(host(b.x_perm)[:R], xs[perm_token]), "x_perm must be an exact gather"
+    x_perm = xs[perm_token]
     a_ref, y_ref = oracle.grouped_swiglu(x_perm, offsets, ex)
     if R:
         a_gpu, y_gpu = host(b.a)[:R], host(b.y_perm)[:R]
@@ -93,13 +94,40 @@ def test_small_layer_parity(shape):
         run.free()
 
 
+@pytest.mark.parametrize("idx", [1, 3, 6])
+def test_materialized_gather_matches_fused(idx):
+    """moe_permute with an x_perm buffer gathers exactly; the gate/up GEMM on that
+    copy gives bit-identical results to the GEMM reading x through perm_token."""
+    shape = SMALL[idx]
+    inp = minp.LayerInputs(shape, seed=2)
+    fused = GpuRun(inp).run()
+    run = GpuRun(inp, gathered=True)
+    out = run.run()
+    run_state["bufs"] = run.bufs
+    try:
+        R = int(out["offsets"][-1])                  # perm_token rows past R are not written
+        for key in fused:
+            a, b = np.asarray(fused[key]), np.asarray(out[key])
+            if key == "perm_token":
+                a, b = a[:R], b[:R]
+            assert np.array_equal(a, b), key
+        full_check(inp, out)
+    finally:
+        run_state.clear()
+        run.free()
+
+
 def test_determinism_two_runs_bitwise():
     inp = minp.LayerInputs(SMALL[4], seed=3)
     run = GpuRun(inp)
     a = run.run()
     b = run.run()
+    R = int(a["offsets"][-1])
     for key in a:
-        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+        u, v = np.asarray(a[key]), np.asarray(b[key])
+        if key == "perm_token":
+            u, v = u[:R], v[:R]
+        assert np.array_equal(u, v), key
     run.free()
 
 
@@ -148,10 +176,20 @@ def test_grouped_gemm_hand_made_groups(dtype):
     a = torch.full((max_rows, F), 7.0, dtype=td, device="cuda")
     y = torch.full((max_rows, d), 7.0, dtype=td, device="cuda")
     off = torch.from_numpy(offsets).cuda()
-    _lib.moe_grouped_swiglu(dev(xp), off, G, max_rows, d, F, dev(wg), dev(wu), dev(wd), a, y)
+    _lib.moe_grouped_swiglu(dev(xp), None, 0, off, G, max_rows, d, F, dev(wg), dev(wu), dev(wd), a, y)
     torch.cuda.synchronize()
     a_ref, y_ref = oracle.grouped_swiglu(xp, offsets, lambda e: (wg[e], wu[e], wd[e]))
     R = int(offsets[-1])
     assert max_rel(host(a)[:R], a_ref) <= TOL[dtype]
     assert max_rel(host(y)[:R], y_ref) <= TOL[dtype]
     assert (host(a)[R:] == 7.0).all() and (host(y)[R:] == 7.0).all(), "rows outside every group are untouched"
+    # the same rows gathered through a row index from a shuffled source
+    perm = rng.permutation(max_rows).astype(np.int32)
+    src = np.empty_like(xp)
+    src[perm] = xp                                          # xp[r] == src[perm[r]]
+    a2 = torch.full_like(a, 7.0)
+    y2 = torch.full_like(y, 7.0)
+    _lib.moe_grouped_swiglu(dev(src), torch.from_numpy(perm).cuda(), max_rows, off, G, max_rows, d, F, dev(wg),
+                            dev(wu), dev(wd), a2, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, a) and torch.equal(y2, y), "row-index gather must match the materialized rows"
