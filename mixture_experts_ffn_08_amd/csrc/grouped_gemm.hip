@@ -269,6 +269,84 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   }
 }
 
+// Skinny variant for groups of a few rows (decode: about T k / E rows per expert).
+// The weights are streamed once from HBM straight into MFMA operands (no LDS): one
+// block per (group, 64 B rows), each wave 16 B rows (dual: 16 gate rows and the same
+// 16 up rows) against 16-row token tiles, v_mfma_f32_16x16x32_bf16 with the weights
+// as the "A" operand.  In each 128-wide K chunk, lane group q = l / 16 owns the 32
+// contiguous k values 32 q .. 32 q + 31 of its row (64 bytes, four 16-byte loads),
+// fed to the four k-steps of the chunk 8 at a time; both operands use that same k
+// assignment, so the products pair up.  Two chunks are in flight per wave.
+constexpr int SK_ROWS = 16;   // B rows per wave
+constexpr int SK_BN = 64;     // B rows per block
+constexpr int SK_CHUNK = 128; // K per chunk
+
+template <bool DUAL>
+__global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
+    const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
+  const int nblk_n = N / SK_BN;
+  const int g = blockIdx.x / nblk_n, nb = blockIdx.x % nblk_n;
+  const int lo = clamp_off(offsets[g], max_rows), hi = clamp_off(offsets[g + 1], max_rows);
+  if (hi <= lo) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int n_base = nb * SK_BN + wave * SK_ROWS;
+  const uint16_t* bg = B0 + ((size_t)g * N + n_base + r16) * K + 32 * q;
+  const uint16_t* bu = DUAL ? B1 + ((size_t)g * N + n_base + r16) * K + 32 * q : bg;
+  const int nchunks = K / SK_CHUNK;
+  constexpr int NB = DUAL ? 2 : 1;
+
+  for (int t0 = lo; t0 < hi; t0 += 16) {
+    int m = min(t0 + r16, hi - 1);
+    if (a_rows != nullptr) m = min(max(a_rows[m], 0), a_nrows - 1);
+    const uint16_t* ap = A + (size_t)m * K + 32 * q;
+    u32x4 wa[2][NB][4], ta[2][4];
+    auto load = [&](int buf, int c) {
+      const int k0 = c * SK_CHUNK;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wa[buf][0][u] = ld16(bg + k0 + 8 * u);
+        if (DUAL) wa[buf][NB - 1][u] = ld16(bu + k0 + 8 * u);
+        ta[buf][u] = ld16(ap + k0 + 8 * u);
+      }
+    };
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load(0, 0);
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load(1, c + 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = mfma16x16x32(as_bf16x8(wa[0][b][u]), as_bf16x8(ta[0][u]), acc[b]);
+      if (c + 1 >= nchunks) break;
+      if (c + 2 < nchunks) load(0, c + 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          acc[b] = mfma16x16x32(as_bf16x8(wa[1][b][u]), as_bf16x8(ta[1][u]), acc[b]);
+    }
+    // acc element i of lane l: B row n_base + 4 (l / 16) + i, token row t0 + l % 16.
+    const int row = t0 + r16;
+    if (row < hi) {
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = acc[0][i];
+        v[i] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[NB - 1][i] : x;
+      }
+      const uint32_t p0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      const uint32_t p1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(C + (size_t)row * N + n_base + 4 * q) = make_uint2(p0, p1);
+    }
+  }
+}
+
 // fp32 path: one thread per output element, plain K loop.
 template <bool DUAL>
 __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __restrict__ A,
@@ -307,6 +385,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
+  if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
+    // few rows per group on average: stream the weights, skip the 256-row tiles
+    const int64_t blocks = (int64_t)a.G * (a.N / SK_BN);
+    if (dual)
+      hipLaunchKernelGGL(grouped_gemm_skinny_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const uint16_t*)a.B0, (const uint16_t*)a.B1, (uint16_t*)a.C);
+    else
+      hipLaunchKernelGGL(grouped_gemm_skinny_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                         (const uint16_t*)a.B0, nullptr, (uint16_t*)a.C);
+    return hipGetLastError();
+  }
   if (a.dtype == MOE_BF16) {
     const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
     const int64_t m_tiles = (a.max_rows + BM - 1) / BM + std::min(a.G, a.max_rows);

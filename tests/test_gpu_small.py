@@ -154,16 +154,19 @@ def test_zero_tokens_is_a_no_op():
     run.free()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_grouped_gemm_hand_made_groups(dtype):
-    """Groups with 0, 1, 127, 128, 129 and 300 rows, rows left outside every group,
+@pytest.mark.parametrize("dtype,sizes", [
+    ("bf16", [0, 1, 127, 128, 129, 300]),                      # 256-row tile kernel
+    ("f32", [0, 1, 127, 128, 129, 300]),
+    ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7]),  # few rows per group: skinny kernel
+])
+def test_grouped_gemm_hand_made_groups(dtype, sizes):
+    """Ragged groups (empty, single row, tile edges), rows left outside every group,
     called directly through the C ABI."""
     rng = np.random.default_rng(4)
     d, F = (256, 384) if dtype == "bf16" else (40, 24)
-    sizes = [0, 1, 127, 128, 129, 300]
     G = len(sizes)
     offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
-    max_rows = int(offsets[-1]) + 37                       # 37 rows beyond the last group
+    max_rows = int(offsets[-1]) + (37 if max(sizes) > 64 else 3)  # rows beyond the last group
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
 
     def mk(shape, scale):
