@@ -43,45 +43,63 @@ __global__ __launch_bounds__(kBP) void hist_kernel(const int32_t* __restrict__ i
 
 // One block of 1024 threads.  tpe threads per expert split the block list into
 // contiguous chunks; chunk sums are scanned in LDS, then each thread writes the
-// running base of its blocks.
+// running base of its blocks; the kept counts are then scanned over experts in
+// LDS for the offsets.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
                                                      int E, int tpe, int64_t cap,
                                                      int32_t* __restrict__ block_base,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets) {
   __shared__ int part[1024];
-  __shared__ int kept_s[MOE_MAX_EXPERTS];
+  __shared__ int kept_s[2][MOE_MAX_EXPERTS];
+  constexpr int kBatch = 16;  // loads in flight per thread
   const int tid = threadIdx.x;
   const int e = tid / tpe, c = tid % tpe;
-  const int chunk = (nblk + tpe - 1) / tpe;
-  const int b0 = min(c * chunk, nblk), b1 = min(b0 + chunk, nblk);
   const bool active = e < E;
+  const int chunk = (nblk + tpe - 1) / tpe;
+  const int b0 = min(c * chunk, nblk), b1 = active ? min(b0 + chunk, nblk) : b0;
+  const int ec = active ? e : 0;
+  // Batches of clamped loads with the out-of-range terms zeroed: no branch
+  // around a load, so a batch waits once.
   int sum = 0;
-  if (active)
-    for (int b = b0; b < b1; ++b) sum += block_counts[(size_t)b * E + e];
+  for (int b = b0; b < b1; b += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) v[q] = block_counts[(size_t)min(b + q, b1 - 1) * E + ec];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) sum += b + q < b1 ? v[q] : 0;
+  }
   part[tid] = sum;
   __syncthreads();
-  if (active) {
-    int base = 0;
+  int base = 0;
+  if (active)
     for (int q = 0; q < c; ++q) base += part[e * tpe + q];
-    for (int b = b0; b < b1; ++b) {
-      block_base[(size_t)b * E + e] = base;
-      base += block_counts[(size_t)b * E + e];
+  for (int b = b0; b < b1; b += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) v[q] = block_counts[(size_t)min(b + q, b1 - 1) * E + ec];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (b + q < b1) {
+        block_base[(size_t)(b + q) * E + ec] = base;
+        base += v[q];
+      }
     }
-    if (c == tpe - 1) {
-      counts[e] = base;
-      kept_s[e] = cap < 0 ? base : (int)min((int64_t)base, cap);
-    }
+  }
+  if (active && c == tpe - 1) {
+    counts[e] = base;
+    kept_s[0][e] = cap < 0 ? base : (int)min((int64_t)base, cap);
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    offsets[0] = 0;
-    for (int q = 0; q < E; ++q) {
-      run += kept_s[q];
-      offsets[q + 1] = run;
-    }
+  // inclusive scan of kept counts over experts (Hillis-Steele, ping-pong buffers)
+  int src = 0;
+  for (int h = 1; h < E; h <<= 1) {
+    if (tid < E) kept_s[src ^ 1][tid] = kept_s[src][tid] + (tid >= h ? kept_s[src][tid - h] : 0);
+    __syncthreads();
+    src ^= 1;
   }
+  if (tid < E) offsets[tid + 1] = kept_s[src][tid];
+  if (tid == 0) offsets[0] = 0;
 }
 
 __global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ idx, int64_t P, int k, int E,

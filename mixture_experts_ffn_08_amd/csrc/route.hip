@@ -6,8 +6,14 @@
 // router": softmax over all experts, keep the k most probable, renormalize over
 // them.  Transformers & Math 17.2: the two softmax orders.
 //
-// One block of 4 waves takes 64 tokens and every expert (E <= 256, padded to
-// EP = 16*NB).
+// Two launch shapes, chosen by T (bf16):
+//  * many tokens: one block of 4 waves takes 64 tokens and every expert (E <= 256,
+//    padded to EP = 16*NB); scores and selection in one kernel (below).
+//  * few tokens (T <= MOE_ROUTE_SPLIT_MAX_T): a grid over (16 tokens, 16 experts)
+//    tiles whose 8 waves each take every 8th 128-wide slice of d, summed in wave
+//    order through LDS, writes the scores; a second kernel selects from them.  At
+//    decode sizes this spreads the router matrix over many CUs instead of one.
+// The fused shape:
 //  * Scores (bf16): a 64 x EP MFMA GEMM (16x16x32 bf16, fp32 accumulate).  Each
 //    wave owns 16 tokens; router-weight chunks of 256 k-values (128 for E > 128)
 //    are staged in a double-buffered LDS ring shared by the 4 waves, and the next
@@ -23,7 +29,14 @@
 namespace moe {
 namespace {
 
-constexpr int kTokens = 64;   // tokens per block
+constexpr int kTokens = 64;   // tokens per block of the fused kernel
+
+#ifndef MOE_ROUTE_SPLIT_MAX_T
+#define MOE_ROUTE_SPLIT_MAX_T 2048
+#endif
+constexpr int kSplitWaves = 8;    // waves per block of the split score kernel
+constexpr int kSplitTile = 16;    // tokens and experts per block of the split score kernel
+constexpr int kSelectTokens = 16; // tokens per block of the select kernel
 
 // K chunk per pipeline stage: large enough that each stage keeps many bytes in
 // flight (a stage round trip is latency-bound), small enough for two stages of
@@ -54,18 +67,20 @@ __device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi) {
   if (beats(oo, oi, bo, bi)) { bo = oo; bi = oi; }
 }
 
-// Top-k for the 64 tokens of a score tile.  Wave w takes tokens 16w .. 16w+15,
-// four at a time (one per 16-lane row).  NB keys per lane; SPL result slots per
-// lane (slot j lives in lane j % 16, register j / 16).
-template <int NB, int SPL>
+// Top-k for 16 * PASSES tokens of a score tile (LDS, or the score rows in global
+// memory).  Each pass gives every 16-lane row of the 4 waves one token: tile row
+// 16 pass + 4 wave + row.  NB keys per lane; SPL result slots per lane (slot j
+// lives in lane j % 16, register j / 16).  WRITE_SCORES copies the tile rows to
+// the score output.
+template <int NB, int SPL, int PASSES, bool WRITE_SCORES>
 __device__ void select_tile(const float* tile, int stride, int t0, int T, int E, int k, int mode, int renorm,
                             float* __restrict__ logits, int32_t* __restrict__ topk_idx,
                             float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, row = lane >> 4;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int lr = wave * 16 + pass * 4 + row;
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int lr = pass * 16 + wave * 4 + row;
     const int t = t0 + lr;
     const bool live = t < T;
     const float* s = tile + lr * stride;
@@ -75,10 +90,10 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
     for (int i = 0; i < NB; ++i) {
       const int e = r + 16 * i;
       const bool present = e < E;
-      const float v = present ? s[e] : 0.f;
+      const float v = (present && live) ? s[e] : 0.f;
       kf[i] = v;
       ko[i] = present ? max(order_key(v), 1u) : 0u;  // 0 marks "absent or taken"
-      if (present && live) logits[(size_t)t * E + e] = v;
+      if (WRITE_SCORES && present && live) logits[(size_t)t * E + e] = v;
     }
     const int rounds = k < E ? k + 1 : k;
     uint32_t my_idx[SPL];
@@ -214,7 +229,75 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     for (int i = 0; i < 4; ++i) tile[(wave * 16 + 4 * kg + i) * L::kTileStride + n] = acc[nb][i] + b;
   }
   __syncthreads();
-  select_tile<NB, SPL>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie);
+  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w,
+                                near_tie);
+}
+
+// Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
+// experts 16 j .. 16 j + 15.  MFMA 16x16x32 with operands loaded straight from
+// global memory: in a 128-wide slice of d, lane group q (lanes 16q .. 16q+15)
+// holds k values 32q .. 32q+31 of its row, 8 per k-step (the same order on both
+// operands, so each product pairs matching k).  Wave w takes slices w, w + 8, ...;
+// the 8 partial tiles are added in wave order, then the bias.
+__global__ __launch_bounds__(kSplitWaves * 64) void route_scores_split_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias, int T,
+    int d, int E, float* __restrict__ logits) {
+  __shared__ f32x4 red[kSplitWaves][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane >> 4, r = lane & 15;
+  const int t0 = blockIdx.x * kSplitTile, e0 = blockIdx.y * kSplitTile;
+  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * d + 32 * q;
+  const uint16_t* wrow = wr + (size_t)min(e0 + r, E - 1) * d + 32 * q;
+  const int nslices = d / 128;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = wave; c0 < nslices; c0 += 2 * kSplitWaves) {
+    const int c1 = c0 + kSplitWaves;
+    const bool two = c1 < nslices;  // uniform over the wave
+    const int c1c = two ? c1 : c0;
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a0[s] = ld16(xrow + c0 * 128 + 8 * s);
+      b0[s] = ld16(wrow + c0 * 128 + 8 * s);
+      a1[s] = ld16(xrow + c1c * 128 + 8 * s);
+      b1[s] = ld16(wrow + c1c * 128 + 8 * s);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(a0[s]), as_bf16x8(b0[s]), acc);
+    if (two) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(a1[s]), as_bf16x8(b1[s]), acc);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 sum = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < kSplitWaves; ++w) sum += red[w][lane];
+    // accumulator element i: token 4q + i of the tile, expert r
+    const int e = e0 + r;
+    if (e < E) {
+      const float b = bias != nullptr ? bias[e] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * q + i;
+        if (t < T) logits[(size_t)t * E + e] = sum[i] + b;
+      }
+    }
+  }
+}
+
+// Selection from the score rows written by route_scores_split_kernel.
+template <int NB, int SPL>
+__global__ __launch_bounds__(256) void route_select_kernel(int T, int E, int k, int mode, int renorm,
+                                                           const float* __restrict__ scores,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w,
+                                                           int32_t* __restrict__ near_tie) {
+  const int t0 = blockIdx.x * kSelectTokens;
+  select_tile<NB, SPL, kSelectTokens / 16, false>(scores + (size_t)t0 * E, E, t0, T, E, k, mode, renorm, nullptr,
+                                                  topk_idx, topk_w, near_tie);
 }
 
 template <int NB, int SPL>
@@ -239,13 +322,20 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     tile[lr * L::kTileStride + n] = acc;
   }
   __syncthreads();
-  select_tile<NB, SPL>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie);
+  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w,
+                                near_tie);
 }
 
 template <int NB, int SPL>
 hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
   const dim3 grid((a.T + kTokens - 1) / kTokens), block(256);
-  if (a.dtype == MOE_BF16)
+  if (a.dtype == MOE_BF16 && a.T <= MOE_ROUTE_SPLIT_MAX_T) {
+    const dim3 sgrid((a.T + kSplitTile - 1) / kSplitTile, (a.E + kSplitTile - 1) / kSplitTile);
+    hipLaunchKernelGGL(route_scores_split_kernel, sgrid, dim3(kSplitWaves * 64), 0, stream,
+                       (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.logits);
+    hipLaunchKernelGGL((route_select_kernel<NB, SPL>), dim3((a.T + kSelectTokens - 1) / kSelectTokens), block, 0,
+                       stream, a.T, a.E, a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
+  } else if (a.dtype == MOE_BF16)
     hipLaunchKernelGGL((route_bf16_kernel<NB, SPL>), grid, block, 0, stream, (const uint16_t*)a.x,
                        (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
                        a.topk_idx, a.topk_w, a.near_tie);

@@ -7,7 +7,7 @@
 //
 // stats_partial_kernel: 64 tokens per block; per-token softmax normalizers, then
 // per-expert sums over the block's tokens in token order -> partial[block][E].
-// stats_final_kernel: one block; sums the partials in block order (fp64), then
+// stats_final_kernel: one block; sums the partials (fp64) in a fixed order, then
 // f, P, L_aux and max/mean.  No atomics: results are deterministic.
 #include "common.h"
 #include "kernels.h"
@@ -15,20 +15,46 @@
 namespace moe {
 namespace {
 
+// Thread groups for the per-expert sums: G = 256 / E groups of E threads (one
+// group when E > 128); group g takes every G-th item, and the G partial sums are
+// added in group order.
+__device__ __forceinline__ int expert_groups(int E) { return E > 128 ? 1 : 256 / E; }
+
 // One block per 64 tokens.  The block's 64 x E score tile is copied to LDS with
 // all loads in flight; each 16-lane row of a wave then takes one token (max and
-// sum of exponentials with DPP butterflies), and finally thread e sums
-// exp(s[t][e] - max_t) / sum_t over the 64 tokens in token order.
+// sum of exponentials with DPP butterflies); finally thread (g, e) sums
+// exp(s[t][e] - max_t) / sum_t over the tokens t = g, g + G, ... of the block.
 __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits, int T, int E,
                                                              float* __restrict__ partial) {
   __shared__ float tile[kStatsTokens * (MOE_MAX_EXPERTS + 1)];
   __shared__ float s_max[kStatsTokens], s_inv[kStatsTokens];
+  __shared__ float red[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kStatsTokens;
   const int nt = min(kStatsTokens, T - t0);
   const int stride = E + 1;
   const float* src = logits + (size_t)t0 * E;
-  for (int i = tid; i < nt * E; i += 256) tile[(i / E) * stride + i % E] = src[i];
+  // All loads of the tile are issued before any is stored (at most 64 per thread).
+  constexpr int kMaxPerThread = kStatsTokens * MOE_MAX_EXPERTS / 256;
+  const int n = nt * E;
+  float v[kMaxPerThread];
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) {
+    v[j] = src[min(tid + 256 * j, n - 1)];  // n >= 1: the block has at least one token
+  }
+  // element i = tid + 256 j sits at (i / E, i % E); step that position by 256 each time
+  int row = tid / E, col = tid % E;
+  const int drow = 256 / E, dcol = 256 % E;
+#pragma unroll
+  for (int j = 0; j < kMaxPerThread; ++j) {
+    if (tid + 256 * j < n) tile[row * stride + col] = v[j];
+    row += drow;
+    col += dcol;
+    if (col >= E) {
+      col -= E;
+      ++row;
+    }
+  }
   __syncthreads();
   const int r = lane & 15;
   for (int lt = wave * 4 + (lane >> 4); lt < kStatsTokens; lt += 16) {  // 16 tokens per pass
@@ -46,27 +72,60 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += 256) {
+  const int G = expert_groups(E);
+  const int g = tid / E, e = tid % E;
+  if (g < G) {
     float acc = 0.f;
-    for (int lt = 0; lt < nt; ++lt) acc += expf(tile[lt * stride + e] - s_max[lt]) * s_inv[lt];
-    partial[(size_t)blockIdx.x * E + e] = acc;
+    for (int lt = g; lt < nt; lt += G) acc += expf(tile[lt * stride + e] - s_max[lt]) * s_inv[lt];
+    red[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < E) {
+    float acc = red[tid];
+    for (int q = 1; q < G; ++q) acc += red[q * E + tid];
+    partial[(size_t)blockIdx.x * E + tid] = acc;
   }
 }
 
+// One block.  Thread (g, e) sums partial[b][e] over blocks b = g, g + G, ... in
+// fp64, 16 loads in flight (indices clamped, out-of-range terms zeroed, no
+// branch around a load); the group sums are added in group order.  Then f, P,
+// L_aux and max/mean.  No atomics: results are deterministic.
 __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restrict__ counts,
                                                            const float* __restrict__ partial, int nblk, int T,
                                                            int k, int E, float alpha, float* __restrict__ f,
                                                            float* __restrict__ P, float* __restrict__ l_aux,
                                                            float* __restrict__ max_over_mean) {
+  __shared__ double s_part[256];
   __shared__ double s_fp[256];
   __shared__ int s_max[256];
-  const int e = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int G = expert_groups(E);
+  const int g = tid / E, ge = tid % E;
+  if (g < G) {
+    double part[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) part[q] = 0.0;
+    for (int b0 = g; b0 < nblk; b0 += 16 * G) {
+      float pv[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) pv[q] = partial[(size_t)min(b0 + q * G, nblk - 1) * E + ge];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) part[q] += b0 + q * G < nblk ? (double)pv[q] : 0.0;
+    }
+    double sum = 0.0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sum += part[q];
+    s_part[tid] = sum;
+  }
+  __syncthreads();
+  const int e = tid;
   const float tk = (float)((int64_t)T * k);
   double fp = 0.0;
   int c = 0;
   if (e < E) {
-    double sum = 0.0;
-    for (int b = 0; b < nblk; ++b) sum += (double)partial[(size_t)b * E + e];
+    double sum = s_part[e];
+    for (int q = 1; q < G; ++q) sum += s_part[q * E + e];
     const float p = (float)(sum / (double)T);
     c = counts[e];
     const float fi = (float)c / tk;
@@ -77,10 +136,10 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restr
   s_fp[e] = fp;
   s_max[e] = c;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (e < s) {
-      s_fp[e] += s_fp[e + s];
-      s_max[e] = max(s_max[e], s_max[e + s]);
+  for (int h = 128; h > 0; h >>= 1) {
+    if (e < h) {
+      s_fp[e] += s_fp[e + h];
+      s_max[e] = max(s_max[e], s_max[e + h]);
     }
     __syncthreads();
   }

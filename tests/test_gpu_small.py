@@ -30,6 +30,9 @@ SMALL = [
     S("E256", "bf16", 130, 128, 256, 8, 128, 0, SM_TK, True, None, True),
     S("k_over_64", "bf16", 40, 128, 200, 70, 128, 0, TK_SM, False, None, False),
     S("tiny_capacity_f32", "f32", 64, 64, 8, 2, 128, 0, TK_SM, False, 1.25, False),
+    # above the router's few-token threshold: scores and selection in one kernel
+    S("many_tokens", "bf16", 2100, 128, 16, 4, 128, 0, SM_TK, True, None, False),
+    S("many_tokens_E200_k70", "bf16", 2070, 128, 200, 70, 128, 0, TK_SM, False, None, False),
 ]
 
 
