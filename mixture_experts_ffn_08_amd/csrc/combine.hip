@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     if (BF16) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        o[q] = (uint32_t)f32_to_bf16(acc[2 * q]) | ((uint32_t)f32_to_bf16(acc[2 * q + 1]) << 16);
+        o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);

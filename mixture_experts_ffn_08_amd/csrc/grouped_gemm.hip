@@ -22,10 +22,13 @@
 //    step of MFMA work.  One barrier per step, a plain s_barrier (a __syncthreads
 //    fence would also wait for the loads in flight).  LDS rows padded to 144 bytes:
 //    conflict-free ds_read_b128.  Within a step, the fragments of the next 16-wide
-//    k slice are read while the current one is multiplied.
+//    k slice are read while the current one is multiplied, and the step's global
+//    loads and LDS writes are spread between the MFMAs (one wave per SIMD: a wave
+//    stalled on issuing a burst of loads leaves its MFMA unit idle).
 //  * MFMA operands swapped (weights as the "A" input), so each lane's accumulators
-//    hold 4 consecutive output columns: the epilogue packs them into 8-byte stores;
-//    SiLU(gate) * up is applied there in fp32.
+//    hold 4 consecutive output columns.  The epilogue applies SiLU(gate) * up in
+//    fp32, rounds to bf16 (v_cvt_pk_bf16_f32), stages the tile in LDS and stores
+//    whole rows.
 //  * Tiles of all groups are enumerated on the device from offsets (no host round
 //    trip); hardware block ids are remapped so that each XCD (blocks are dealt
 //    round-robin to the 8 XCDs) works on a contiguous run of tiles: the same expert's
@@ -132,11 +135,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const char* b_base0 = reinterpret_cast<const char*>(B0 + (size_t)g * N * K);
   const char* b_base1 = DUAL ? reinterpret_cast<const char*>(B1 + (size_t)g * N * K) : b_base0;
   uint32_t a_off8[8], b_off8[8];
+  int arow[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
+  if (a_rows != nullptr) {  // gather through the row index: 8 loads in flight, one wait
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = a_rows[arow[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    int r = min(row0 + crow + 32 * i, row_end - 1);
-    if (a_rows != nullptr) r = min(max(a_rows[r], 0), a_nrows - 1);  // gather through the row index
-    a_off8[i] = ((uint32_t)r * (uint32_t)K + ccol) * 2u;
+    a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
     const int br = crow + 32 * i;
     const int nrow = DUAL ? n0 + (br & (BN / 2 - 1)) : min(n0 + br, N - 1);
     b_off8[i] = ((uint32_t)nrow * (uint32_t)K + ccol) * 2u;
@@ -145,14 +156,23 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // Two register sets: the loads of K step kt+2 are issued while step kt is
   // multiplied and step kt+1 is still in flight.
   u32x4 ra[2][8], rb[2][8];
-  auto load = [&](auto set, int k0) {
+  // Quarter q of a K step's loads: A and B chunks 2q and 2q + 1.
+  auto load_part = [&](auto set, int k0, int q) {
     constexpr int S = decltype(set)::value;
-    const uint32_t kb = (uint32_t)k0 * 2u;
+    // the K offset is block-uniform: fold it into the scalar bases
+    const size_t kb = (size_t)k0 * 2u;
+    const char* ak = a_base + kb;
+    const char* bk0 = b_base0 + kb;
+    const char* bk1 = b_base1 + kb;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[S][i] = ld16(a_base + (a_off8[i] + kb));
-      rb[S][i] = ld16((DUAL && i >= 4 ? b_base1 : b_base0) + (b_off8[i] + kb));
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
+      ra[S][i] = ld16(ak + a_off8[i]);
+      rb[S][i] = ld16((DUAL && i >= 4 ? bk1 : bk0) + b_off8[i]);
     }
+  };
+  auto load = [&](auto set, int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_part(set, k0, q);
   };
   auto store = [&](auto set, int stage) {
     constexpr int S = decltype(set)::value;
@@ -214,24 +234,46 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   auto step = [&](auto set, int kt) {
     constexpr int S = decltype(set)::value;
     using Other = std::integral_constant<int, S ^ 1>;
-    load(set, min((kt + 2) * BK, last));
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the step
+    const int kn = min((kt + 2) * BK, last);
     const uint16_t* st = lds + S * STAGE;
+    // The global loads and LDS traffic are spread over the 64 MFMAs: a wave that
+    // issued its 16 loads back to back would stall on the vector memory queue
+    // with its MFMA unit idle.  Per k slice (fenced, so that fragment lifetimes
+    // stay one slice long): 4 loads and the 8 fragment reads of the next slice
+    // (last slice: the 16 LDS writes of the next stage), each load or pair of
+    // LDS operations followed by MFMAs.
+    auto slice_pattern = [&](auto lds_mask, auto lds_n) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+      }
+    };
+    using DsRead = std::integral_constant<int, 0x100>;
+    using DsWrite = std::integral_constant<int, 0x200>;
+    using Two = std::integral_constant<int, 2>;
+    using Four = std::integral_constant<int, 4>;
     read_frags(st, 16, 1);
+    load_part(set, kn, 0);
     mma(0);
+    slice_pattern(DsRead{}, Two{});
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 32, 0);
+    load_part(set, kn, 1);
     mma(1);
+    slice_pattern(DsRead{}, Two{});
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
+    load_part(set, kn, 2);
     mma(0);
-    mma(1);
+    slice_pattern(DsRead{}, Two{});
+    __builtin_amdgcn_sched_barrier(0);
+    load_part(set, kn, 3);
     store(Other{}, S ^ 1);
-    // Order: the 8 fragment reads of k slice s+1, then the 16 MFMAs of slice s.
-    for (int q = 0; q < 3; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // DS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);    // DS writes of the next stage
+    mma(1);
+    slice_pattern(DsWrite{}, Four{});
     lds_barrier();
     read_frags(lds + (S ^ 1) * STAGE, 0, 0);
   };
@@ -240,32 +282,42 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     step(R1{}, kt + 1);
   }
 
-  // Epilogue.  acc[i][j] element r of lane l: output row (m) = 32 i + l % 32 of the
-  // wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of fragment j;
-  // each lane writes 4 consecutive columns (8 bytes).  (Staging the tile through LDS
-  // for full-row writes measured slower.)
-  const int m_base = row0 + wm * 128 + frow;
+  // Epilogue through LDS.  acc[i][j] element r of lane l: output row (m) = 32 i +
+  // l % 32 of the wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of
+  // fragment j.  Stored straight to memory, each store instruction would touch 32
+  // rows with 16 bytes apiece; instead the block's bf16 tile is written to LDS
+  // (row-major, rows padded by 16 bytes) and then stored as whole rows, 16 bytes
+  // per lane, so each instruction writes 8 full 128-byte lines.
+  constexpr int TN = DUAL ? BN / 2 : BN;  // output columns of the block tile
+  constexpr int OST = TN + 8;             // bf16 per LDS output row
+  static_assert(BM * OST <= 2 * STAGE, "output tile must fit in the stage memory");
+  uint16_t* ot = lds;
+  lds_barrier();  // every wave is done with the last stage
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = m_base + i * 32;
-    if (row >= row_end) continue;
-    uint16_t* crow_ptr = C + (size_t)row * N;
+    const int r = wm * 128 + i * 32 + frow;
 #pragma unroll
     for (int j = 0; j < (DUAL ? 2 : 4); ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = (DUAL ? n0 + wn * 64 : n0 + wn * 128) + j * 32 + 8 * q + 4 * half;
-        if (!DUAL && col >= N) continue;
+        const int c = (DUAL ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * half;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = acc[i][j][4 * q + e];
           v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + 2][4 * q + e] : x;
         }
-        const uint32_t p0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-        const uint32_t p1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(crow_ptr + col) = make_uint2(p0, p1);
+        *reinterpret_cast<uint2*>(ot + r * OST + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
+  }
+  lds_barrier();
+  constexpr int CPR = TN / 8;  // 16-byte chunks per output row
+  const int ncols = DUAL ? TN : min(TN, N - n0);
+#pragma unroll 4
+  for (int c = tid; c < BM * CPR; c += 256) {
+    const int r = c / CPR, cc = 8 * (c % CPR);
+    const int row = row0 + r;
+    if (row < row_end && cc < ncols) st16(C + (size_t)row * N + n0 + cc, ld16(ot + r * OST + cc));
   }
 }
 
@@ -340,8 +392,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
         const float x = acc[0][i];
         v[i] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[NB - 1][i] : x;
       }
-      const uint32_t p0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-      const uint32_t p1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      const uint32_t p0 = pack_bf16x2(v[0], v[1]);
+      const uint32_t p1 = pack_bf16x2(v[2], v[3]);
       *reinterpret_cast<uint2*>(C + (size_t)row * N + n_base + 4 * q) = make_uint2(p0, p1);
     }
   }
