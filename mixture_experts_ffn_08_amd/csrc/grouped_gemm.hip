@@ -323,78 +323,121 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 
 // Skinny variant for groups of a few rows (decode: about T k / E rows per expert).
 // The weights are streamed once from HBM straight into MFMA operands (no LDS): one
-// block per (group, 64 B rows), each wave 16 B rows (dual: 16 gate rows and the same
-// 16 up rows) against 16-row token tiles, v_mfma_f32_16x16x32_bf16 with the weights
-// as the "A" operand.  In each 128-wide K chunk, lane group q = l / 16 owns the 32
+// block per (group, 64 B rows; single: 128), each wave two 16-row B sets (dual: 16
+// gate rows and the same 16 up rows; single: 32 consecutive rows) against 16-row
+// token tiles, v_mfma_f32_16x16x32_bf16 with the weights as the "A" operand.  In each 128-wide K chunk, lane group q = l / 16 owns the 32
 // contiguous k values 32 q .. 32 q + 31 of its row (64 bytes, four 16-byte loads),
 // fed to the four k-steps of the chunk 8 at a time; both operands use that same k
 // assignment, so the products pair up.  Two chunks are in flight per wave.
-constexpr int SK_ROWS = 16;   // B rows per wave
-constexpr int SK_BN = 64;     // B rows per block
+constexpr int SK_ROWS = 16;   // B rows per MFMA tile
+// B rows per block: dual, 4 waves x 16 rows (each with its gate and up rows);
+// single, 4 waves x 32 rows (two 16-row sets).
+__host__ __device__ constexpr int sk_bn(bool dual) { return dual ? 64 : 128; }
 constexpr int SK_CHUNK = 128; // K per chunk
 
-template <bool DUAL>
+template <bool DUAL, bool GATHER>
 __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
-  const int nblk_n = N / SK_BN;
+  const int nblk_n = N / sk_bn(DUAL);
   const int g = blockIdx.x / nblk_n, nb = blockIdx.x % nblk_n;
   const int lo = clamp_off(offsets[g], max_rows), hi = clamp_off(offsets[g + 1], max_rows);
   if (hi <= lo) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
-  const int n_base = nb * SK_BN + wave * SK_ROWS;
+  const int n_base = nb * sk_bn(DUAL) + wave * (DUAL ? SK_ROWS : 2 * SK_ROWS);
+  // the two B row sets: dual, gate and up rows n_base ..; single, rows n_base .. and
+  // n_base + 16 ..
   const uint16_t* bg = B0 + ((size_t)g * N + n_base + r16) * K + 32 * q;
-  const uint16_t* bu = DUAL ? B1 + ((size_t)g * N + n_base + r16) * K + 32 * q : bg;
+  const uint16_t* bu = DUAL ? B1 + ((size_t)g * N + n_base + r16) * K + 32 * q : bg + (size_t)SK_ROWS * K;
   const int nchunks = K / SK_CHUNK;
-  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int NB = 2;
 
-  for (int t0 = lo; t0 < hi; t0 += 16) {
-    int m = min(t0 + r16, hi - 1);
-    if (a_rows != nullptr) m = min(max(a_rows[m], 0), a_nrows - 1);
-    const uint16_t* ap = A + (size_t)m * K + 32 * q;
-    u32x4 wa[2][NB][4], ta[2][4];
-    auto load = [&](int buf, int c) {
-      const int k0 = c * SK_CHUNK;
+  // Register sets 0 and 1 hold chunks 2p and 2p + 1, each issued as weights then
+  // tokens, so that waiting for one set leaves the other in flight (the vector
+  // memory counter retires in order).  The loop prefetches the next pair while a
+  // pair is multiplied; the last pair is peeled off, so no load sits under a branch
+  // and none is wasted (an odd chunk count re-loads the last chunk once, as a
+  // second chunk multiplied with zeroed token values).
+  u32x4 wa[2][NB][4], ta[2][4];
+  auto load_w = [&](int buf, int c) {
+    const int k0 = min(c, nchunks - 1) * SK_CHUNK;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wa[buf][0][u] = ld16(bg + k0 + 8 * u);
-        if (DUAL) wa[buf][NB - 1][u] = ld16(bu + k0 + 8 * u);
-        ta[buf][u] = ld16(ap + k0 + 8 * u);
-      }
-    };
+    for (int u = 0; u < 4; ++u) {
+      wa[buf][0][u] = ld16(bg + k0 + 8 * u);
+      wa[buf][1][u] = ld16(bu + k0 + 8 * u);
+    }
+  };
+  auto load_x = [&](int buf, int c, const uint16_t* ap) {
+    const int k0 = min(c, nchunks - 1) * SK_CHUNK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ta[buf][u] = ld16(ap + k0 + 8 * u);
+  };
+  const int npairs = (nchunks + 1) / 2;
+  for (int t0 = lo; t0 < hi; t0 += 16) {
+    // an opaque zero keeps the first loads inside this loop (hoisted, they would be
+    // drained by the first wait)
+    int z;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+    int m = min(t0 + r16, hi - 1);
+    int mg = 0;
+    if (GATHER) mg = a_rows[m];
+    load_w(0, z);
+    if (GATHER) m = min(max(mg, 0), a_nrows - 1);
+    const uint16_t* ap = A + (size_t)m * K + 32 * q;
+    // issue order w0, x0, w1, x1 as in the loop (the scheduler would otherwise
+    // reorder or sink the loads)
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(0, z, ap);
+    int z1 = z + 1;
+    asm volatile("" : "+s"(z1) : "v"(m));  // w1 after x0 (its index "depends" on the row)
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(1, z1);
+    load_x(1, z1, ap);
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load(0, 0);
-    for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) load(1, c + 1);
+    auto mma = [&](int buf, uint32_t keep) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          acc[b] = mfma16x16x32(as_bf16x8(wa[0][b][u]), as_bf16x8(ta[0][u]), acc[b]);
-      if (c + 1 >= nchunks) break;
-      if (c + 2 < nchunks) load(0, c + 2);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = mfma16x16x32(as_bf16x8(wa[1][b][u]), as_bf16x8(ta[1][u]), acc[b]);
+          acc[b] = mfma16x16x32(as_bf16x8(wa[buf][b][u]), as_bf16x8(ta[buf][u] & keep), acc[b]);
+    };
+    for (int p = 0; p + 1 < npairs; ++p) {
+      mma(0, ~0u);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(0, 2 * p + 2);
+      load_x(0, 2 * p + 2, ap);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(1, ~0u);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(1, 2 * p + 3);
+      load_x(1, 2 * p + 3, ap);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // acc element i of lane l: B row n_base + 4 (l / 16) + i, token row t0 + l % 16.
+    mma(0, ~0u);
+    mma(1, 2 * npairs <= nchunks ? ~0u : 0u);  // uniform
+    // acc[b] element i of lane l: B row 4 (l / 16) + i of set b, token row t0 + l % 16.
     const int row = t0 + r16;
     if (row < hi) {
-      float v[4];
+      uint16_t* crow = C + (size_t)row * N + n_base + 4 * q;
+      if (DUAL) {
+        float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = acc[0][i];
-        v[i] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[NB - 1][i] : x;
+        for (int i = 0; i < 4; ++i) {
+          const float x = acc[0][i];
+          v[i] = __fdividef(x, 1.f + __expf(-x)) * acc[1][i];
+        }
+        *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          *reinterpret_cast<uint2*>(crow + b * SK_ROWS) =
+              make_uint2(pack_bf16x2(acc[b][0], acc[b][1]), pack_bf16x2(acc[b][2], acc[b][3]));
       }
-      const uint32_t p0 = pack_bf16x2(v[0], v[1]);
-      const uint32_t p1 = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(C + (size_t)row * N + n_base + 4 * q) = make_uint2(p0, p1);
     }
   }
 }
@@ -439,15 +482,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
   if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
     // few rows per group on average: stream the weights, skip the 256-row tiles
-    const int64_t blocks = (int64_t)a.G * (a.N / SK_BN);
-    if (dual)
-      hipLaunchKernelGGL(grouped_gemm_skinny_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const uint16_t*)a.B0, (const uint16_t*)a.B1, (uint16_t*)a.C);
-    else
-      hipLaunchKernelGGL(grouped_gemm_skinny_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const uint16_t*)a.B0, nullptr, (uint16_t*)a.C);
+    const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
+#define MOE_SKINNY(D, GA)                                                                                    \
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA>), grid, block, 0, stream, (const uint16_t*)a.A,    \
+                     a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,     \
+                     D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C)
+    const bool gather = a.a_rows != nullptr;
+    if (dual && gather) MOE_SKINNY(true, true);
+    else if (dual) MOE_SKINNY(true, false);
+    else if (gather) MOE_SKINNY(false, true);
+    else MOE_SKINNY(false, false);
+#undef MOE_SKINNY
     return hipGetLastError();
   }
   if (a.dtype == MOE_BF16) {
