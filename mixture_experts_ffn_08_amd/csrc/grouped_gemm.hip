@@ -29,10 +29,15 @@
 //    hold 4 consecutive output columns.  The epilogue applies SiLU(gate) * up in
 //    fp32, rounds to bf16 (v_cvt_pk_bf16_f32), stages the tile in LDS and stores
 //    whole rows.
-//  * Tiles of all groups are enumerated on the device from offsets (no host round
-//    trip); hardware block ids are remapped so that each XCD (blocks are dealt
-//    round-robin to the 8 XCDs) works on a contiguous run of tiles: the same expert's
-//    weights and the same rows stay in that XCD's L2.
+//  * Persistent: one block per CU.  Tiles of all groups are enumerated on the
+//    device from offsets (no host round trip); each XCD (blocks are dealt
+//    round-robin to the 8 XCDs) owns a contiguous run of tiles that its blocks take
+//    in turn, so the same expert's weights and the same rows stay in that XCD's L2.
+//    The next tile's first two K steps are loaded while the current tile's output
+//    is stored.
+//  * Global loads are buffer loads (scalar resource, 32-bit lane offset, the K
+//    offset as the scalar offset), which keeps 64-bit per-lane addresses out of the
+//    register budget.
 #include <algorithm>
 #include <type_traits>
 
@@ -46,21 +51,27 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;             // bf16 elements per LDS row (16-byte pad)
 constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
 constexpr int kXcds = 8;
+// Fourth word of a gfx9-family buffer resource: raw (untyped) 32-bit access.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
 
 struct TileScan {
-  int incl[256];  // inclusive prefix of per-group m-tile counts
+  int incl[256];   // inclusive prefix of per-group m-tile counts
+  int start[257];  // clamped group bounds: group g holds rows [start[g], start[g + 1])
   int wave_tot[4];
 };
 
-// Block-wide: per-group m-tile counts and their inclusive prefix; returns the total.
+// Block-wide: per-group m-tile counts, their inclusive prefix and the clamped group
+// bounds; returns the total.
 __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, TileScan& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = 0;
   if (tid < G) {
     const int lo = clamp_off(offsets[tid], max_rows), hi = clamp_off(offsets[tid + 1], max_rows);
     cnt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+    s.start[tid] = lo;
+    if (tid == G - 1) s.start[G] = hi;
   }
   int v = cnt;
 #pragma unroll
@@ -78,8 +89,7 @@ __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_ro
 
 // Group g holding m-tile mt (binary search on the inclusive prefix), its first row
 // and end row.
-__device__ void locate(const int32_t* __restrict__ offsets, int G, int max_rows, const TileScan& s, int mt,
-                       int& g, int& row0, int& row_end) {
+__device__ void locate(int G, const TileScan& s, int mt, int& g, int& row0, int& row_end) {
   int lo = 0, hi = G - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -87,16 +97,8 @@ __device__ void locate(const int32_t* __restrict__ offsets, int G, int max_rows,
   }
   g = lo;
   const int excl = g > 0 ? s.incl[g - 1] : 0;
-  row0 = clamp_off(offsets[g], max_rows) + (mt - excl) * BM;
-  row_end = clamp_off(offsets[g + 1], max_rows);
-}
-
-// Logical tile of hardware block `bid` among `active` live blocks: XCD x = bid % 8
-// takes the x-th contiguous run of the live tiles.
-__device__ __forceinline__ int xcd_remap(int bid, int active) {
-  const int x = bid % kXcds, j = bid / kXcds;
-  const int per = active / kXcds, rem = active % kXcds;
-  return x * per + min(x, rem) + j;
+  row0 = s.start[g] + (mt - excl) * BM;
+  row_end = s.start[g + 1];
 }
 
 // Block barrier without the memory fence of __syncthreads (which would also wait
@@ -113,45 +115,70 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   __shared__ TileScan scan;
 
   const int total = scan_tiles(offsets, G, max_rows, scan) * n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= total) return;
-  const int tile = xcd_remap(bid, total);
-  const int mt = tile / n_tiles, nt = tile % n_tiles;
-  int g, row0, row_end;
-  locate(offsets, G, max_rows, scan, mt, g, row0, row_end);
+  // Persistent schedule.  Hardware block b runs on XCD b % 8 (blocks are dealt
+  // round-robin); XCD x owns the contiguous tile run [x per, (x + 1) per) and its
+  // blocks take the run's tiles in turn, so the CUs of an XCD work on neighbouring
+  // tiles (the same expert's weights, the same rows) at the same time and share
+  // them through that XCD's L2.
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslots = gridDim.x / kXcds;
+  const int per = (total + kXcds - 1) / kXcds;
+  const int run_end = min((xcd + 1) * per, total);
+  int tile = xcd * per + slot;
+  if (tile >= run_end) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  // B rows of this tile: dual -> gate rows [n0, n0+128) then up rows [n0, n0+128);
-  // single -> rows [n0, n0+256) (clamped at N; columns past N are not stored).
-  const int n0 = DUAL ? nt * (BN / 2) : nt * BN;
+  const int nk = K / BK;  // even: K % 128 == 0
 
   // Copy mapping: each operand tile is 256 rows x 8 chunks of 16 bytes; thread tid
   // moves chunks tid + 256 i: row (tid >> 3) + 32 i, k offset 8 (tid & 7).
   // Addresses: block-uniform bases (scalar registers) plus 32-bit byte offsets per
   // thread (the host checks that every operand fits in 4 GiB).
   const int crow = tid >> 3, ccol = 8 * (tid & 7);
-  const char* a_base = reinterpret_cast<const char*>(A);
-  const char* b_base0 = reinterpret_cast<const char*>(B0 + (size_t)g * N * K);
-  const char* b_base1 = DUAL ? reinterpret_cast<const char*>(B1 + (size_t)g * N * K) : b_base0;
-  uint32_t a_off8[8], b_off8[8];
-  int arow[8];
+  // Loads go through buffer resources (a scalar base and size) with a 32-bit lane
+  // offset and the block-uniform K offset as the scalar offset: no 64-bit address
+  // per lane is ever formed (the compiler would otherwise keep 16 of them live).
+  const __amdgpu_buffer_rsrc_t rsrc_a =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((uint32_t)a_nrows * (uint32_t)K * 2u), kBufferFlags);
+  __amdgpu_buffer_rsrc_t rsrc_b0, rsrc_b1;
+  uint32_t a_off8[8];
+  // B chunk i of this thread: row (first row of the tile) + crow + 32 (i & b_mask),
+  // i.e. the lane offset b_lane plus the block-uniform step (i & b_mask) * b_step.
+  const uint32_t b_lane = ((uint32_t)crow * (uint32_t)K + ccol) * 2u;
+  const uint32_t b_step = 32u * (uint32_t)K * 2u;
+  int b_mask;
+  int row0, row_end, n0;
+  // B rows of a tile: dual -> gate rows [n0, n0+128) then up rows [n0, n0+128);
+  // single -> rows [n0, n0+256), or [n0, n0+128) twice for a last tile of 128
+  // columns (the columns past N are not stored).
+  auto setup = [&](int t) {
+    const int mt = t / n_tiles, nt = t % n_tiles;
+    int g;
+    locate(G, scan, mt, g, row0, row_end);
+    g = __builtin_amdgcn_readfirstlane(g);  // block-uniform: keep the bases in scalar registers
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    row_end = __builtin_amdgcn_readfirstlane(row_end);
+    n0 = DUAL ? nt * (BN / 2) : nt * BN;
+    const int b_bytes = (int)((uint32_t)(N - n0) * (uint32_t)K * 2u);  // rows [n0, N) of the expert
+    rsrc_b0 = __builtin_amdgcn_make_buffer_rsrc((void*)(B0 + ((size_t)g * N + n0) * K), (short)0, b_bytes,
+                                                kBufferFlags);
+    rsrc_b1 = DUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(B1 + ((size_t)g * N + n0) * K), (short)0, b_bytes,
+                                                       kBufferFlags)
+                   : rsrc_b0;
+    b_mask = (DUAL || n0 + BN > N) ? 3 : 7;
+    int arow[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
-  if (a_rows != nullptr) {  // gather through the row index: 8 loads in flight, one wait
-    int v[8];
+    for (int i = 0; i < 8; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
+    if (a_rows != nullptr) {  // gather through the row index: 8 loads in flight, one wait
+      int v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = a_rows[arow[i]];
+      for (int i = 0; i < 8; ++i) v[i] = a_rows[arow[i]];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
-  }
+      for (int i = 0; i < 8; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
+    }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
-    const int br = crow + 32 * i;
-    const int nrow = DUAL ? n0 + (br & (BN / 2 - 1)) : min(n0 + br, N - 1);
-    b_off8[i] = ((uint32_t)nrow * (uint32_t)K + ccol) * 2u;
-  }
+    for (int i = 0; i < 8; ++i) a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
+  };
 
   // Two register sets: the loads of K step kt+2 are issued while step kt is
   // multiplied and step kt+1 is still in flight.
@@ -159,15 +186,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // Quarter q of a K step's loads: A and B chunks 2q and 2q + 1.
   auto load_part = [&](auto set, int k0, int q) {
     constexpr int S = decltype(set)::value;
-    // the K offset is block-uniform: fold it into the scalar bases
-    const size_t kb = (size_t)k0 * 2u;
-    const char* ak = a_base + kb;
-    const char* bk0 = b_base0 + kb;
-    const char* bk1 = b_base1 + kb;
+    const int kb = k0 * 2;
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      ra[S][i] = ld16(ak + a_off8[i]);
-      rb[S][i] = ld16((DUAL && i >= 4 ? bk1 : bk0) + b_off8[i]);
+      ra[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (int)a_off8[i], kb, 0));
+      rb[S][i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(DUAL && i >= 4 ? rsrc_b1 : rsrc_b0, (int)b_lane,
+                                                       kb + (int)((i & b_mask) * b_step), 0));
     }
   };
   auto load = [&](auto set, int k0) {
@@ -186,13 +211,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   };
 
   f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   // Fragment offsets inside a stage: A rows wm*128 + 32 i; B rows per the layout above.
   const int frow = lane & 31, half = lane >> 5, fk = 8 * half;
   int a_off[4], b_off[4];
@@ -220,21 +238,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
-  const int nk = K / BK;  // even: K % 128 == 0
-  load(R0{}, 0);
-  load(R1{}, min(BK, (nk - 1) * BK));
-  store(R0{}, 0);
-  lds_barrier();
-  read_frags(lds, 0, 0);
   // Step kt: stage kt & 1 is in LDS, register set kt & 1 is free again, set
-  // (kt + 1) & 1 holds step kt+1 in flight.  The step has no branches (a join
-  // would make the compiler's wait counts drain the set just issued): past the end
-  // it re-loads the last K chunk, and what that writes to LDS is never read.
-  const int last = (nk - 1) * BK;
-  auto step = [&](auto set, int kt) {
+  // (kt + 1) & 1 holds step kt+1 in flight.  Modes: kFull loads step kt+2 and
+  // stores step kt+1 to the other stage; kNoLoad (step nk-2) only stores; kLast
+  // (step nk-1) neither, and leaves the final barrier to the epilogue.  No step has
+  // a branch (a join would make the compiler's wait counts drain the loads just
+  // issued).
+  constexpr int kFull = 0, kNoLoad = 1, kLast = 2;
+  auto step = [&](auto set, int kt, auto mode) {
     constexpr int S = decltype(set)::value;
+    constexpr int MODE = decltype(mode)::value;
     using Other = std::integral_constant<int, S ^ 1>;
-    const int kn = min((kt + 2) * BK, last);
+    const int kn = (kt + 2) * BK;
     const uint16_t* st = lds + S * STAGE;
     // The global loads and LDS traffic are spread over the 64 MFMAs: a wave that
     // issued its 16 loads back to back would stall on the vector memory queue
@@ -245,79 +260,118 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
+        if constexpr (MODE == kFull) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
+        if constexpr (decltype(lds_n)::value > 0)
+          __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
         __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
       }
     };
     using DsRead = std::integral_constant<int, 0x100>;
     using DsWrite = std::integral_constant<int, 0x200>;
+    using Zero = std::integral_constant<int, 0>;
     using Two = std::integral_constant<int, 2>;
     using Four = std::integral_constant<int, 4>;
     read_frags(st, 16, 1);
-    load_part(set, kn, 0);
+    if constexpr (MODE == kFull) load_part(set, kn, 0);
     mma(0);
     slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 32, 0);
-    load_part(set, kn, 1);
+    if constexpr (MODE == kFull) load_part(set, kn, 1);
     mma(1);
     slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
-    load_part(set, kn, 2);
+    if constexpr (MODE == kFull) load_part(set, kn, 2);
     mma(0);
     slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
-    load_part(set, kn, 3);
-    store(Other{}, S ^ 1);
+    if constexpr (MODE == kFull) load_part(set, kn, 3);
+    if constexpr (MODE != kLast) store(Other{}, S ^ 1);
     mma(1);
-    slice_pattern(DsWrite{}, Four{});
-    lds_barrier();
-    read_frags(lds + (S ^ 1) * STAGE, 0, 0);
+    if constexpr (MODE != kLast) {
+      slice_pattern(DsWrite{}, Four{});
+      lds_barrier();
+      read_frags(lds + (S ^ 1) * STAGE, 0, 0);
+    } else {
+      slice_pattern(DsWrite{}, Zero{});
+    }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(R0{}, kt);
-    step(R1{}, kt + 1);
-  }
 
-  // Epilogue through LDS.  acc[i][j] element r of lane l: output row (m) = 32 i +
-  // l % 32 of the wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of
-  // fragment j.  Stored straight to memory, each store instruction would touch 32
-  // rows with 16 bytes apiece; instead the block's bf16 tile is written to LDS
-  // (row-major, rows padded by 16 bytes) and then stored as whole rows, 16 bytes
-  // per lane, so each instruction writes 8 full 128-byte lines.
-  constexpr int TN = DUAL ? BN / 2 : BN;  // output columns of the block tile
+  using Full = std::integral_constant<int, kFull>;
+  using NoLoad = std::integral_constant<int, kNoLoad>;
+  using Last = std::integral_constant<int, kLast>;
+  constexpr int TN = DUAL ? BN / 2 : BN;  // output columns of a block tile
   constexpr int OST = TN + 8;             // bf16 per LDS output row
   static_assert(BM * OST <= 2 * STAGE, "output tile must fit in the stage memory");
-  uint16_t* ot = lds;
-  lds_barrier();  // every wave is done with the last stage
+
+  setup(tile);
+  load(R0{}, 0);
+  load(R1{}, BK);
+  for (;;) {
+    lds_barrier();  // the stage memory is free (the previous tile's epilogue is done with it)
+    store(R0{}, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wm * 128 + i * 32 + frow;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < (DUAL ? 2 : 4); ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = (DUAL ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * half;
-        float v[4];
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    lds_barrier();
+    read_frags(lds, 0, 0);
+    for (int kt = 0; kt < nk - 2; kt += 2) {
+      step(R0{}, kt, Full{});
+      step(R1{}, kt + 1, Full{});
+    }
+    step(R0{}, nk - 2, NoLoad{});
+    step(R1{}, nk - 1, Last{});
+
+    // Epilogue through LDS.  acc[i][j] element r of lane l: output row (m) = 32 i +
+    // l % 32 of the wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of
+    // fragment j.  Stored straight to memory, each store instruction would touch 32
+    // rows with 16 bytes apiece; instead the block's bf16 tile is written to LDS
+    // (row-major, rows padded by 16 bytes) and then stored as whole rows, 16 bytes
+    // per lane, so each instruction writes 8 full 128-byte lines.
+    uint16_t* ot = lds;
+    lds_barrier();  // every wave is done with the last stage
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = acc[i][j][4 * q + e];
-          v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + 2][4 * q + e] : x;
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + frow;
+#pragma unroll
+      for (int j = 0; j < (DUAL ? 2 : 4); ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = (DUAL ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * half;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = acc[i][j][4 * q + e];
+            v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + 2][4 * q + e] : x;
+          }
+          *reinterpret_cast<uint2*>(ot + r * OST + c) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
-        *reinterpret_cast<uint2*>(ot + r * OST + c) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      }
-  }
-  lds_barrier();
-  constexpr int CPR = TN / 8;  // 16-byte chunks per output row
-  const int ncols = DUAL ? TN : min(TN, N - n0);
+    }
+    // The next tile's first two K steps are loaded while this tile's rows are
+    // stored (the block's last tile re-loads itself: no load sits under a branch).
+    const int e_row0 = row0, e_row_end = row_end, e_n0 = n0;
+    const int next = tile + nslots;
+    const bool more = next < run_end;
+    setup(more ? next : tile);
+    load(R0{}, 0);
+    load(R1{}, BK);
+    lds_barrier();
+    constexpr int CPR = TN / 8;  // 16-byte chunks per output row
+    const int ncols = DUAL ? TN : min(TN, N - e_n0);
 #pragma unroll 4
-  for (int c = tid; c < BM * CPR; c += 256) {
-    const int r = c / CPR, cc = 8 * (c % CPR);
-    const int row = row0 + r;
-    if (row < row_end && cc < ncols) st16(C + (size_t)row * N + n0 + cc, ld16(ot + r * OST + cc));
+    for (int c = tid; c < BM * CPR; c += 256) {
+      const int r = c / CPR, cc = 8 * (c % CPR);
+      const int row = e_row0 + r;
+      if (row < e_row_end && cc < ncols) st16(C + (size_t)row * N + e_n0 + cc, ld16(ot + r * OST + cc));
+    }
+    if (!more) break;
+    tile = next;
   }
 }
 
@@ -479,6 +533,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
 
 }  // namespace
 
+// Blocks of the persistent kernel: the current device's compute units, rounded
+// down to a multiple of the XCD count (256 on MI355X), cached per device.
+int persistent_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < kXcds)
+      cus = 256;
+    cached[dev] = cus / kXcds * kXcds;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
   if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
     // few rows per group on average: stream the weights, skip the 256-row tiles
@@ -498,8 +567,11 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   if (a.dtype == MOE_BF16) {
     const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
     const int64_t m_tiles = (a.max_rows + BM - 1) / BM + std::min(a.G, a.max_rows);
-    const int64_t blocks = m_tiles * n_tiles;
-    if (blocks <= 0) return hipSuccess;
+    // persistent grid: one block per CU (the LDS stages take a CU), a multiple of
+    // the 8 XCDs, no more than the tiles there can be
+    const int64_t max_tiles = m_tiles * n_tiles;
+    if (max_tiles <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
     if (dual)
       hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                          (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
