@@ -379,10 +379,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 // The weights are streamed once from HBM straight into MFMA operands (no LDS): one
 // block per (group, 64 B rows; single: 128), each wave two 16-row B sets (dual: 16
 // gate rows and the same 16 up rows; single: 32 consecutive rows) against 16-row
-// token tiles, v_mfma_f32_16x16x32_bf16 with the weights as the "A" operand.  In each 128-wide K chunk, lane group q = l / 16 owns the 32
-// contiguous k values 32 q .. 32 q + 31 of its row (64 bytes, four 16-byte loads),
-// fed to the four k-steps of the chunk 8 at a time; both operands use that same k
-// assignment, so the products pair up.  Two chunks are in flight per wave.
+// token tiles, v_mfma_f32_16x16x32_bf16 with the weights as the "A" operand.  In
+// k-step u of a 128-wide K chunk, lane group q = l / 16 holds k values
+// 32 u + 8 q .. 32 u + 8 q + 7 of its row (the instruction's own order), so each
+// 16-byte load instruction reads 64 contiguous bytes of 16 rows.  Two chunks are
+// in flight per wave.
 constexpr int SK_ROWS = 16;   // B rows per MFMA tile
 // B rows per block: dual, 4 waves x 16 rows (each with its gate and up rows);
 // single, 4 waves x 32 rows (two 16-row sets).
@@ -403,8 +404,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
   const int n_base = nb * sk_bn(DUAL) + wave * (DUAL ? SK_ROWS : 2 * SK_ROWS);
   // the two B row sets: dual, gate and up rows n_base ..; single, rows n_base .. and
   // n_base + 16 ..
-  const uint16_t* bg = B0 + ((size_t)g * N + n_base + r16) * K + 32 * q;
-  const uint16_t* bu = DUAL ? B1 + ((size_t)g * N + n_base + r16) * K + 32 * q : bg + (size_t)SK_ROWS * K;
+  const uint16_t* bg = B0 + ((size_t)g * N + n_base + r16) * K + 8 * q;
+  const uint16_t* bu = DUAL ? B1 + ((size_t)g * N + n_base + r16) * K + 8 * q : bg + (size_t)SK_ROWS * K;
   const int nchunks = K / SK_CHUNK;
   constexpr int NB = 2;
 
@@ -419,14 +420,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const int k0 = min(c, nchunks - 1) * SK_CHUNK;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      wa[buf][0][u] = ld16(bg + k0 + 8 * u);
-      wa[buf][1][u] = ld16(bu + k0 + 8 * u);
+      wa[buf][0][u] = ld16(bg + k0 + 32 * u);
+      wa[buf][1][u] = ld16(bu + k0 + 32 * u);
     }
   };
   auto load_x = [&](int buf, int c, const uint16_t* ap) {
     const int k0 = min(c, nchunks - 1) * SK_CHUNK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ta[buf][u] = ld16(ap + k0 + 8 * u);
+    for (int u = 0; u < 4; ++u) ta[buf][u] = ld16(ap + k0 + 32 * u);
   };
   const int npairs = (nchunks + 1) / 2;
   for (int t0 = lo; t0 < hi; t0 += 16) {
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     if (GATHER) mg = a_rows[m];
     load_w(0, z);
     if (GATHER) m = min(max(mg, 0), a_nrows - 1);
-    const uint16_t* ap = A + (size_t)m * K + 32 * q;
+    const uint16_t* ap = A + (size_t)m * K + 8 * q;
     // issue order w0, x0, w1, x1 as in the loop (the scheduler would otherwise
     // reorder or sink the loads)
     __builtin_amdgcn_sched_barrier(0);

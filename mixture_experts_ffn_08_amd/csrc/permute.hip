@@ -14,6 +14,7 @@
 //   scan_kernel   one block: per-expert scan over blocks, demand counts,
 //                 capacity, exclusive scan over experts -> offsets
 //   rank_kernel   bitmap ranks -> row_of, perm_token
+//   permute_single_kernel   the three above in one block when T k <= 512
 //   gather_kernel x_perm[r] = x[perm_token[r]], one wave per row, 16-byte lanes
 #include <algorithm>
 
@@ -160,6 +161,59 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
   }
 }
 
+// All of histogram, scan and rank in one block, for T k <= 512 assignments (the
+// decode shapes): the same results as the three kernels above with one block.
+__global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __restrict__ idx, int64_t P, int k,
+                                                              int E, int64_t cap, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ row_of,
+                                                              int32_t* __restrict__ perm_token) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  __shared__ int kept[MOE_MAX_EXPERTS];
+  __shared__ int incl[2][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kBP) mask[i] = 0u;
+  for (int i = tid; i < E; i += kBP) cnt[i] = 0;
+  __syncthreads();
+  const int e = tid < P ? idx[tid] : -1;
+  const bool valid = (unsigned)e < (unsigned)E;
+  const int w = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid) {
+    atomicOr(&mask[e * kWords + w], bit);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < E; i += kBP) {
+    counts[i] = cnt[i];
+    kept[i] = cap < 0 ? cnt[i] : (int)min((int64_t)cnt[i], cap);
+    incl[0][i] = kept[i];
+  }
+  __syncthreads();
+  // inclusive scan of the kept counts over experts (Hillis-Steele, ping-pong buffers)
+  int src = 0;
+  for (int h = 1; h < E; h <<= 1) {
+    for (int i = tid; i < E; i += kBP) incl[src ^ 1][i] = incl[src][i] + (i >= h ? incl[src][i - h] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  for (int i = tid; i < E; i += kBP) offsets[i + 1] = incl[src][i];
+  if (tid == 0) offsets[0] = 0;
+  if (tid >= P) return;
+  int32_t row = -1;
+  if (valid) {
+    const uint32_t* m = mask + e * kWords;
+    int rank = __popc(m[w] & (bit - 1u));
+    for (int q = 0; q < w; ++q) rank += __popc(m[q]);
+    if (cap < 0 || rank < cap) {
+      row = incl[src][e] - kept[e] + rank;
+      perm_token[row] = tid / k;
+    }
+  }
+  row_of[tid] = row;
+}
+
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
@@ -168,11 +222,16 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   int ep = 1;
   while (ep < a.E) ep <<= 1;
   const int tpe = min(64, 1024 / ep);
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, tpe,
-                     a.capacity, a.block_base, a.counts, a.offsets);
-  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
-                     a.block_base, a.offsets, a.row_of, a.perm_token);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
+                       a.counts, a.offsets, a.row_of, a.perm_token);
+  } else {
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, tpe,
+                       a.capacity, a.block_base, a.counts, a.offsets);
+    hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
+                       a.block_base, a.offsets, a.row_of, a.perm_token);
+  }
   if (a.x_perm == nullptr) return hipGetLastError();
   const int max_rows = (int)P;
   const int blocks = (int)std::min<int64_t>((max_rows + 3) / 4, 8192);

@@ -235,9 +235,10 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
 // experts 16 j .. 16 j + 15.  MFMA 16x16x32 with operands loaded straight from
-// global memory: in a 128-wide slice of d, lane group q (lanes 16q .. 16q+15)
-// holds k values 32q .. 32q+31 of its row, 8 per k-step (the same order on both
-// operands, so each product pairs matching k).  Wave w takes slices w, w + 8, ...;
+// global memory: in k-step s of a 128-wide slice of d, lane group q (lanes
+// 16q .. 16q+15) holds k values 32s + 8q .. 32s + 8q + 7 of its row (the
+// instruction's own order), so each load instruction reads 64 contiguous bytes of
+// 16 rows.  Wave w takes slices w, w + 8, ...;
 // the 8 partial tiles are added in wave order, then the bias.
 __global__ __launch_bounds__(kSplitWaves * 64) void route_scores_split_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias, int T,
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(kSplitWaves * 64) void route_scores_split_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, r = lane & 15;
   const int t0 = blockIdx.x * kSplitTile, e0 = blockIdx.y * kSplitTile;
-  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * d + 32 * q;
-  const uint16_t* wrow = wr + (size_t)min(e0 + r, E - 1) * d + 32 * q;
+  const uint16_t* xrow = x + (size_t)min(t0 + r, T - 1) * d + 8 * q;
+  const uint16_t* wrow = wr + (size_t)min(e0 + r, E - 1) * d + 8 * q;
   const int nslices = d / 128;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = wave; c0 < nslices; c0 += 2 * kSplitWaves) {
@@ -257,10 +258,10 @@ __global__ __launch_bounds__(kSplitWaves * 64) void route_scores_split_kernel(
     u32x4 a0[4], b0[4], a1[4], b1[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      a0[s] = ld16(xrow + c0 * 128 + 8 * s);
-      b0[s] = ld16(wrow + c0 * 128 + 8 * s);
-      a1[s] = ld16(xrow + c1c * 128 + 8 * s);
-      b1[s] = ld16(wrow + c1c * 128 + 8 * s);
+      a0[s] = ld16(xrow + c0 * 128 + 32 * s);
+      b0[s] = ld16(wrow + c0 * 128 + 32 * s);
+      a1[s] = ld16(xrow + c1c * 128 + 32 * s);
+      b1[s] = ld16(wrow + c1c * 128 + 32 * s);
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(a0[s]), as_bf16x8(b0[s]), acc);

@@ -8,7 +8,8 @@
 // stats_partial_kernel: 64 tokens per block; per-token softmax normalizers, then
 // per-expert sums over the block's tokens in token order -> partial[block][E].
 // stats_final_kernel: one block; sums the partials (fp64) in a fixed order, then
-// f, P, L_aux and max/mean.  No atomics: results are deterministic.
+// f, P, L_aux and max/mean.  When T fits one block, the partial kernel finishes
+// in place.  No atomics: results are deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,12 +21,53 @@ namespace {
 // added in group order.
 __device__ __forceinline__ int expert_groups(int E) { return E > 128 ? 1 : 256 / E; }
 
+// Block-wide finish: thread e < E holds sum_t softmax(s_t)_e in fp64.  Writes f, P,
+// L_aux = alpha E sum_e f_e P_e and max/mean = E max_e counts_e / (T k).
+__device__ void finish_stats(double sum, const int32_t* __restrict__ counts, int T, int k, int E, float alpha,
+                             float* __restrict__ f, float* __restrict__ P, float* __restrict__ l_aux,
+                             float* __restrict__ max_over_mean) {
+  __shared__ double s_fp[256];
+  __shared__ int s_max[256];
+  const int e = threadIdx.x;
+  const float tk = (float)((int64_t)T * k);
+  double fp = 0.0;
+  int c = 0;
+  if (e < E) {
+    const float p = (float)(sum / (double)T);
+    c = counts[e];
+    const float fi = (float)c / tk;
+    f[e] = fi;
+    P[e] = p;
+    fp = (double)fi * (double)p;
+  }
+  s_fp[e] = fp;
+  s_max[e] = c;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (e < h) {
+      s_fp[e] += s_fp[e + h];
+      s_max[e] = max(s_max[e], s_max[e + h]);
+    }
+    __syncthreads();
+  }
+  if (e == 0) {
+    *l_aux = (float)((double)alpha * (double)E * s_fp[0]);
+    *max_over_mean = (float)((int64_t)E * s_max[0]) / tk;
+  }
+}
+
 // One block per 64 tokens.  The block's 64 x E score tile is copied to LDS with
 // all loads in flight; each 16-lane row of a wave then takes one token (max and
 // sum of exponentials with DPP butterflies); finally thread (g, e) sums
 // exp(s[t][e] - max_t) / sum_t over the tokens t = g, g + G, ... of the block.
+// FINAL (one block covers all T tokens): finish in place instead of writing partials.
+template <bool FINAL>
 __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restrict__ logits, int T, int E,
-                                                             float* __restrict__ partial) {
+                                                             float* __restrict__ partial,
+                                                             const int32_t* __restrict__ counts, int k,
+                                                             float alpha, float* __restrict__ f,
+                                                             float* __restrict__ P, float* __restrict__ l_aux,
+                                                             float* __restrict__ max_over_mean) {
   __shared__ float tile[kStatsTokens * (MOE_MAX_EXPERTS + 1)];
   __shared__ float s_max[kStatsTokens], s_inv[kStatsTokens];
   __shared__ float red[256];
@@ -80,11 +122,13 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
     red[tid] = acc;
   }
   __syncthreads();
+  float acc = 0.f;
   if (tid < E) {
-    float acc = red[tid];
+    acc = red[tid];
     for (int q = 1; q < G; ++q) acc += red[q * E + tid];
-    partial[(size_t)blockIdx.x * E + tid] = acc;
+    if (!FINAL) partial[(size_t)blockIdx.x * E + tid] = acc;
   }
+  if (FINAL) finish_stats((double)acc, counts, T, k, E, alpha, f, P, l_aux, max_over_mean);
 }
 
 // One block.  Thread (g, e) sums partial[b][e] over blocks b = g, g + G, ... in
@@ -97,8 +141,6 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restr
                                                            float* __restrict__ P, float* __restrict__ l_aux,
                                                            float* __restrict__ max_over_mean) {
   __shared__ double s_part[256];
-  __shared__ double s_fp[256];
-  __shared__ int s_max[256];
   const int tid = threadIdx.x;
   const int G = expert_groups(E);
   const int g = tid / E, ge = tid % E;
@@ -119,41 +161,25 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restr
     s_part[tid] = sum;
   }
   __syncthreads();
-  const int e = tid;
-  const float tk = (float)((int64_t)T * k);
-  double fp = 0.0;
-  int c = 0;
-  if (e < E) {
-    double sum = s_part[e];
-    for (int q = 1; q < G; ++q) sum += s_part[q * E + e];
-    const float p = (float)(sum / (double)T);
-    c = counts[e];
-    const float fi = (float)c / tk;
-    f[e] = fi;
-    P[e] = p;
-    fp = (double)fi * (double)p;
+  double sum = 0.0;
+  if (tid < E) {
+    sum = s_part[tid];
+    for (int q = 1; q < G; ++q) sum += s_part[q * E + tid];
   }
-  s_fp[e] = fp;
-  s_max[e] = c;
-  __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (e < h) {
-      s_fp[e] += s_fp[e + h];
-      s_max[e] = max(s_max[e], s_max[e + h]);
-    }
-    __syncthreads();
-  }
-  if (e == 0) {
-    *l_aux = (float)((double)alpha * (double)E * s_fp[0]);
-    *max_over_mean = (float)((int64_t)E * s_max[0]) / tk;
-  }
+  finish_stats(sum, counts, T, k, E, alpha, f, P, l_aux, max_over_mean);
 }
 
 }  // namespace
 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream) {
   const int nblk = stats_blocks(a.T);
-  hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, stream, a.logits, a.T, a.E, a.partial);
+  if (nblk == 1) {
+    hipLaunchKernelGGL(stats_partial_kernel<true>, dim3(1), dim3(256), 0, stream, a.logits, a.T, a.E, nullptr,
+                       a.counts, a.k, a.alpha, a.f, a.P, a.l_aux, a.max_over_mean);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(stats_partial_kernel<false>, dim3(nblk), dim3(256), 0, stream, a.logits, a.T, a.E, a.partial,
+                     nullptr, a.k, a.alpha, nullptr, nullptr, nullptr, nullptr);
   hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(256), 0, stream, a.counts, a.partial, nblk, a.T, a.k,
                      a.E, a.alpha, a.f, a.P, a.l_aux, a.max_over_mean);
   return hipGetLastError();
