@@ -13,7 +13,8 @@
  * Conventions for every entry point:
  *   - Pointers named as device pointers must point to device memory (HBM) of
  *     the current device; the caller owns and allocates every buffer.  The
- *     library keeps no state and allocates nothing.
+ *     library allocates nothing; its only state is a per-device cache of the
+ *     compute-unit count (read once with hipDeviceGetAttribute).
  *   - Tensors are dense, row-major.  Rows of x and of the weights must start on
  *     16-byte boundaries (true when the base is 16-byte aligned and d, F are
  *     multiples of 8).
@@ -77,6 +78,9 @@ enum moe_score_mode {
  *   logit_bias device [E] float32 or NULL added to every token's scores before
  *                                        selection and softmax
  *   logits     device [T][E] float32 out  s = x W_r^T (+ bias), float32 accumulation
+ *                                        (the summation order depends on T: up to
+ *                                        2048 bf16 tokens take a split-d kernel;
+ *                                        results are deterministic for given T)
  *   topk_idx   device [T][k] int32 out    the k highest scores, best first; equal
  *                                        scores go to the lower expert index
  *   topk_w     device [T][k] float32 out  gate weights by `mode`; with
