@@ -7,9 +7,9 @@
 //
 // One wave per token; each lane owns 16-byte column chunks.  Rows are gathered
 // (no atomics) and summed in slot order in fp32, then rounded once: the result is
-// deterministic.  The loads of all k slots (and the shared row) for a chunk are
-// issued before any arithmetic, so a wave keeps k + 1 loads in flight; k is a
-// template parameter for the common values.
+// deterministic.  The loads of all k slots (and the shared row) for up to 4 chunks
+// are issued before any arithmetic, so a lane keeps up to 4 (k + 1) loads in
+// flight; k is a template parameter for the common values.
 #include "common.h"
 #include "kernels.h"
 
@@ -30,8 +30,12 @@ __device__ __forceinline__ void accumulate(float* acc, const u32x4 v, float w) {
   }
 }
 
-// KT > 0: k known at compile time; KT == 0: runtime k (any value).
-template <bool BF16, int KT>
+// KT > 0: k known at compile time; KT == 0: runtime k (any value).  With KT > 0
+// the token's slot rows and weights are read once, and the slot loads of up to
+// kChunksPerLane 16-byte chunks per lane are all issued before any is summed.
+constexpr int kChunksPerLane = 4;
+
+template <bool BF16, int KT, bool SHARED>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_perm,
                                                        const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ topk_w,
@@ -47,50 +51,87 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
   const char* yp = static_cast<const char*>(y_perm);
   const char* sh = static_cast<const char*>(shared_y);
-  for (int c = lane; c < chunks; c += 64) {
-    float acc[EPC];
+  char* yt = static_cast<char*>(y) + (size_t)t * row_bytes;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if constexpr (KT > 0) {
+    // A dropped slot reads row 0 (y_perm has T k >= 1 rows) and its values are
+    // replaced by zeros after the load: no load sits under a branch.
+    const char* src[KT];
+    float w[KT];
+    bool kept[KT];
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if constexpr (KT > 0) {
-      u32x4 v[KT];
-      float w[KT];
+    for (int j = 0; j < KT; ++j) {
+      const int r = __builtin_amdgcn_readfirstlane(row_of[(size_t)t * KT + j]);
+      kept[j] = r >= 0 && r < rows;
+      w[j] = kept[j] ? topk_w[(size_t)t * KT + j] : 0.f;
+      src[j] = yp + (size_t)(kept[j] ? r : 0) * row_bytes;
+    }
+    const char* shrow = SHARED ? sh + (size_t)t * row_bytes : nullptr;
+    for (int c0 = lane; c0 < chunks; c0 += 64 * kChunksPerLane) {
+      u32x4 v[kChunksPerLane][KT], vs[kChunksPerLane];
 #pragma unroll
-      for (int j = 0; j < KT; ++j) {
-        const int r = row_of[(size_t)t * KT + j];
-        const bool kept = r >= 0 && r < rows;
-        w[j] = kept ? topk_w[(size_t)t * KT + j] : 0.f;
-        v[j] = kept ? ld16(yp + (size_t)r * row_bytes + (size_t)c * 16) : zero;
+      for (int u = 0; u < kChunksPerLane; ++u) {
+        const size_t off = (size_t)min(c0 + 64 * u, chunks - 1) * 16;  // past the end: re-read, not stored
+#pragma unroll
+        for (int j = 0; j < KT; ++j) v[u][j] = ld16(src[j] + off);
+        if (SHARED) vs[u] = ld16(shrow + off);
       }
 #pragma unroll
-      for (int j = 0; j < KT; ++j) accumulate<BF16>(acc, v[j], w[j]);
-    } else {
+      for (int u = 0; u < kChunksPerLane; ++u) {
+        const int c = c0 + 64 * u;
+        float acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KT; ++j) accumulate<BF16>(acc, kept[j] ? v[u][j] : zero, w[j]);
+        if (SHARED) accumulate<BF16>(acc, vs[u], 1.f);
+        u32x4 o;
+        if (BF16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+        }
+        if (c < chunks) st16(yt + (size_t)c * 16, o);
+      }
+    }
+  } else {
+    for (int c = lane; c < chunks; c += 64) {
+      float acc[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
       for (int j = 0; j < k; ++j) {
         const int r = row_of[(size_t)t * k + j];
         if (r < 0 || r >= rows) continue;
         accumulate<BF16>(acc, ld16(yp + (size_t)r * row_bytes + (size_t)c * 16), topk_w[(size_t)t * k + j]);
       }
-    }
-    if (sh != nullptr) accumulate<BF16>(acc, ld16(sh + (size_t)t * row_bytes + (size_t)c * 16), 1.f);
-    u32x4 o;
-    if (BF16) {
+      if (SHARED) accumulate<BF16>(acc, ld16(sh + (size_t)t * row_bytes + (size_t)c * 16), 1.f);
+      u32x4 o;
+      if (BF16) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-    } else {
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+      }
+      st16(yt + (size_t)c * 16, o);
     }
-    st16(static_cast<char*>(y) + (size_t)t * row_bytes + (size_t)c * 16, o);
   }
 }
 
 template <bool BF16>
 hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid((a.T + 3) / 4), block(256);
-#define MOE_COMBINE(KT)                                                                                 \
-  hipLaunchKernelGGL((combine_kernel<BF16, KT>), grid, block, 0, stream, a.y_perm, a.row_of, a.topk_w, \
-                     a.shared_y, a.T, a.k, a.d, a.y)
+#define MOE_COMBINE(KT)                                                                                       \
+  do {                                                                                                        \
+    if (a.shared_y != nullptr)                                                                                \
+      hipLaunchKernelGGL((combine_kernel<BF16, KT, true>), grid, block, 0, stream, a.y_perm, a.row_of,      \
+                         a.topk_w, a.shared_y, a.T, a.k, a.d, a.y);                                           \
+    else                                                                                                      \
+      hipLaunchKernelGGL((combine_kernel<BF16, KT, false>), grid, block, 0, stream, a.y_perm, a.row_of,     \
+                         a.topk_w, nullptr, a.T, a.k, a.d, a.y);                                              \
+  } while (0)
   switch (a.k) {
     case 1: MOE_COMBINE(1); break;
     case 2: MOE_COMBINE(2); break;
