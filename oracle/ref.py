@@ -33,8 +33,13 @@ notes of the repository):
   * P_i is the mean of the softmax over all E experts in every score mode
     ([MIN] load_balancing_loss takes the full softmax although its router
     softmaxes only the chosen k).
-  * Selection is on the float32 router scores; equal scores go to the lower
-    expert index; slots are ordered by descending score.
+  * Selection is on float32 keys: the router scores, sigmoid(scores) in the
+    sigmoid mode, or, with a selection bias, softmax(s) + b / s + b /
+    sigmoid(s) + b by mode (the [RS] listing adds the bias to the softmax
+    probabilities).  Equal keys go to the lower expert index; slots are ordered
+    by descending key.
+  * In the sigmoid mode the weights are the chosen sigmoid scores normalized over
+    the chosen k, always ([RS] "The router"); P_i stays the mean softmax.
   * An expert over capacity keeps the tokens that reach it first in ascending
     token order; a dropped slot contributes nothing and the token's other
     weights are not renormalized ([TM] 17.5; [MIN] "Capacity factor").
@@ -51,6 +56,7 @@ import numpy as np
 
 SOFTMAX_THEN_TOPK = 0
 TOPK_THEN_SOFTMAX = 1
+SIGMOID_THEN_TOPK = 2
 NEAR_TIE_GAP = 1e-4
 
 
@@ -96,6 +102,37 @@ def softmax(s: np.ndarray, axis: int = -1) -> np.ndarray:
     return z / z.sum(axis=axis, keepdims=True)
 
 
+def sigmoid(s: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-s)), float64."""
+    return 1.0 / (1.0 + np.exp(-np.asarray(s, np.float64)))
+
+
+def selection_keys(scores: np.ndarray, mode: int, select_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """What top-k ranks, per token and expert.
+
+    Without a selection bias: the score itself (softmax and top-k-first modes;
+    softmax is monotonic, so ranking the probabilities ranks the scores), or
+    sigmoid(score) in the sigmoid mode.
+    With a selection bias b ([RS] "Keeping the load even", bias balancing, and the
+    MoE listing's balance="bias": the bias is added only to what chooses the
+    top k, never to the weights): softmax(s) + b, s + b (top-k-first), or
+    sigmoid(s) + b.  Returned as float32, the precision the selection runs in."""
+    s = np.asarray(scores, np.float64)
+    if select_bias is None:
+        key = sigmoid(s) if mode == SIGMOID_THEN_TOPK else s
+    else:
+        b = np.asarray(select_bias, np.float64)[None, :]
+        if mode == SOFTMAX_THEN_TOPK:
+            key = softmax(s) + b
+        elif mode == TOPK_THEN_SOFTMAX:
+            key = s + b
+        elif mode == SIGMOID_THEN_TOPK:
+            key = sigmoid(s) + b
+        else:
+            raise ValueError(f"unknown score mode {mode}")
+    return key.astype(np.float32)
+
+
 def top_k(scores: np.ndarray, k: int):
     """The k experts with the highest scores per token ([MIN] Router: logits.topk;
     [RS] the MoE listing: topk over the scores).  Ties go to the lower expert
@@ -121,25 +158,48 @@ def gate_weights(scores: np.ndarray, idx: np.ndarray, mode: int, renorm: bool) -
     softmax); with renorm, w_j = p_j / sum over the chosen p ([RS] "The router"
     equation and worked example).
     TOPK_THEN_SOFTMAX: w = softmax over the chosen k scores alone ([TM] 17.2,
-    Mixtral; [MIN] Router; [LT] gate equation)."""
+    Mixtral; [MIN] Router; [LT] gate equation).
+    SIGMOID_THEN_TOPK: g = sigmoid(s) per expert and w_j = g_j / sum over the
+    chosen g ([RS] "The router": DeepSeek-V3 scores with a sigmoid, normalized
+    over the chosen experts); renorm does not apply.
+    The weights use the scores only: a selection bias never enters them."""
     s = np.asarray(scores, np.float64)
+    ii = idx.astype(np.int64)
     if mode == SOFTMAX_THEN_TOPK:
         p = softmax(s)
-        w = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+        w = np.take_along_axis(p, ii, axis=1)
         if renorm:
             w = w / w.sum(axis=1, keepdims=True)
     elif mode == TOPK_THEN_SOFTMAX:
-        w = softmax(np.take_along_axis(s, idx.astype(np.int64), axis=1))
+        w = softmax(np.take_along_axis(s, ii, axis=1))
+    elif mode == SIGMOID_THEN_TOPK:
+        g = np.take_along_axis(sigmoid(s), ii, axis=1)
+        w = g / g.sum(axis=1, keepdims=True)
     else:
         raise ValueError(f"unknown score mode {mode}")
     return w.astype(np.float32)
 
 
-def route(x, w_router, bias, k: int, mode: int, renorm: bool):
-    """Router step: (scores[T][E] f32, idx[T][k] i32, w[T][k] f32, near_tie[T] i32)."""
+def route(x, w_router, bias, k: int, mode: int, renorm: bool, select_bias=None):
+    """Router step: (scores[T][E] f32, idx[T][k] i32, w[T][k] f32, near_tie[T] i32).
+    near_tie refers to the selection keys (selection_keys)."""
     s = router_scores(x, w_router, bias)
-    idx, near = top_k(s, k)
+    idx, near = top_k(selection_keys(s, mode, select_bias), k)
     return s, idx, gate_weights(s, idx, mode, renorm), near
+
+
+def bias_update(select_bias: np.ndarray, counts: np.ndarray, T: int, k: int, rate: float) -> np.ndarray:
+    """One step of bias balancing ([RS] "Keeping the load even", and the MoE
+    listing's update after each step): raise b_e by a fixed amount when expert e
+    got fewer than its share of the T k assignments, lower it when it got more,
+    leave it when it got exactly its share.  f_e = counts_e / (T k) is compared
+    with 1/E exactly (as integers: T k against E counts_e); the update is the
+    float32 sum b_e + rate * sign, as the listing's float32 buffer computes it."""
+    b = np.asarray(select_bias, np.float32)
+    counts = np.asarray(counts, np.int64)
+    E = b.shape[0]
+    sign = np.sign(np.int64(T) * k - E * counts).astype(np.float32)
+    return (b + np.float32(rate) * sign).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------
@@ -288,7 +348,7 @@ def balance_stats(counts, scores, T: int, k: int, E: int, alpha: float):
 # Whole layer.
 
 def layer_forward(x, w_router, bias, expert_weights, shared_weights, *, k: int, mode: int,
-                  renorm: bool, phi: Optional[float], alpha: float, dtype: str):
+                  renorm: bool, phi: Optional[float], alpha: float, dtype: str, select_bias=None):
     """The full layer, step by step, returning every intermediate.
 
     x, w_router: stored values (float32 arrays).  expert_weights(e) ->
@@ -297,7 +357,7 @@ def layer_forward(x, w_router, bias, expert_weights, shared_weights, *, k: int, 
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
-    s, idx, w, near = route(x, w_router, bias, k, mode, renorm)
+    s, idx, w, near = route(x, w_router, bias, k, mode, renorm, select_bias)
     cap = capacity(T, k, E, phi)
     counts, offsets, row_of, perm_token = dispatch(idx, E, cap)
     x_perm = permute_rows(x, perm_token)

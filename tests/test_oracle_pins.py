@@ -90,6 +90,119 @@ def test_near_tie_flag():
     assert near_full.tolist() == [0, 0]
 
 
+# ------------------------------------------- selection bias and sigmoid ----
+
+def test_sigmoid_matches_scipy_expit():
+    s = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(oracle.sigmoid(s), scipy.special.expit(s), rtol=1e-14, atol=0)
+
+
+def test_sigmoid_mode_weights():
+    """[RS] "The router": sigmoid scores normalized over the chosen experts."""
+    rng = np.random.default_rng(11)
+    s = rng.normal(size=(300, 12)).astype(np.float32)
+    # without a bias the sigmoid ranks exactly as the scores do (monotonic)
+    idx, _ = oracle.top_k(oracle.selection_keys(s, oracle.SIGMOID_THEN_TOPK), 4)
+    idx_s, _ = oracle.top_k(s, 4)
+    assert np.array_equal(idx, idx_s)
+    w = oracle.gate_weights(s, idx, oracle.SIGMOID_THEN_TOPK, renorm=False)
+    g = scipy.special.expit(np.take_along_axis(s.astype(np.float64), idx.astype(np.int64), 1))
+    np.testing.assert_allclose(w, g / g.sum(1, keepdims=True), rtol=1e-6)
+    # renorm does not apply: the weights are always normalized over the chosen k
+    np.testing.assert_array_equal(w, oracle.gate_weights(s, idx, oracle.SIGMOID_THEN_TOPK, renorm=True))
+    # k = 1: the single weight is 1
+    i1, _ = oracle.top_k(oracle.selection_keys(s, oracle.SIGMOID_THEN_TOPK), 1)
+    assert np.all(oracle.gate_weights(s, i1, oracle.SIGMOID_THEN_TOPK, renorm=False) == 1.0)
+    # a zero router: every sigmoid score is 1/2, the k lowest experts win, equal weights
+    z = np.zeros((3, 8), np.float32)
+    iz, near = oracle.top_k(oracle.selection_keys(z, oracle.SIGMOID_THEN_TOPK), 3)
+    assert (iz == [0, 1, 2]).all() and (near == 1).all()
+    np.testing.assert_allclose(oracle.gate_weights(z, iz, oracle.SIGMOID_THEN_TOPK, False), 1 / 3, rtol=1e-7)
+
+
+def test_selection_bias_changes_choice_not_weights(golden):
+    """[RS] "Keeping the load even": the bias is added to the scores only when
+    choosing the top k, never to the weights.  On the worked example a bias of 0.2
+    on the third expert makes it beat the second; the weights are the router's own
+    probabilities of the chosen two, renormalized."""
+    g = golden("router_worked_example.txt")
+    probs = np.array(g["probs"], np.float64)
+    s = np.log(probs).astype(np.float32)[None, :]
+    b = np.array([0.0, 0.0, 0.2, 0.0], np.float32)
+    keys = oracle.selection_keys(s, oracle.SOFTMAX_THEN_TOPK, b)
+    idx, _ = oracle.top_k(keys, 2)
+    assert idx[0].tolist() == [0, 2]
+    w = oracle.gate_weights(s, idx, oracle.SOFTMAX_THEN_TOPK, renorm=True)
+    np.testing.assert_allclose(w[0], [0.5 / 0.65, 0.15 / 0.65], rtol=1e-6)
+    # a zero bias selects what the scores select
+    rng = np.random.default_rng(12)
+    r = rng.normal(size=(200, 10)).astype(np.float32)
+    for mode in (oracle.SOFTMAX_THEN_TOPK, oracle.TOPK_THEN_SOFTMAX, oracle.SIGMOID_THEN_TOPK):
+        i0, _ = oracle.top_k(oracle.selection_keys(r, mode, np.zeros(10, np.float32)), 3)
+        i1, _ = oracle.top_k(r, 3)
+        assert np.array_equal(i0, i1)
+    # a large bias puts its expert first for every token, weights still from the scores
+    big = np.zeros(10, np.float32)
+    big[7] = 10.0
+    for mode in (oracle.SOFTMAX_THEN_TOPK, oracle.TOPK_THEN_SOFTMAX, oracle.SIGMOID_THEN_TOPK):
+        ib, _ = oracle.top_k(oracle.selection_keys(r, mode, big), 3)
+        assert (ib[:, 0] == 7).all()
+    ib, _ = oracle.top_k(oracle.selection_keys(r, oracle.TOPK_THEN_SOFTMAX, big), 3)
+    wb = oracle.gate_weights(r, ib, oracle.TOPK_THEN_SOFTMAX, renorm=False)
+    ch = np.take_along_axis(r.astype(np.float64), ib.astype(np.int64), 1)
+    np.testing.assert_allclose(wb, scipy.special.softmax(ch, axis=1), rtol=1e-6)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_selection_bias_brute_force_over_subsets(mode):
+    """The chosen set maximizes the sum of the biased keys (brute force over all
+    subsets of 7 experts choose 3)."""
+    rng = np.random.default_rng(13 + mode)
+    s = rng.normal(size=(150, 7)).astype(np.float32)
+    b = (rng.normal(size=7) * 0.3).astype(np.float32)
+    keys = oracle.selection_keys(s, mode, b)
+    idx, _ = oracle.top_k(keys, 3)
+    sd = s.astype(np.float64)
+    base = {0: scipy.special.softmax(sd, axis=1), 1: sd, 2: scipy.special.expit(sd)}[mode]
+    full = base + b.astype(np.float64)[None, :]
+    for t in range(s.shape[0]):
+        best = max(itertools.combinations(range(7), 3), key=lambda c: sum(full[t, list(c)]))
+        assert sorted(idx[t].tolist()) == list(best)
+
+
+def test_bias_update_sign_rule():
+    """[RS]: raise the bias of an expert that got fewer than its share, lower it
+    for one that got more, leave one that got exactly its share."""
+    b = np.array([0.5, 0.5, 0.5, 0.5], np.float32)
+    # T k = 8 over E = 4: a share of 2 each
+    nb = oracle.bias_update(b, np.array([3, 1, 2, 2]), T=4, k=2, rate=0.25)
+    assert nb.tolist() == [0.25, 0.75, 0.5, 0.5]
+    # T k = 10 over E = 3: a share of 3 1/3, so 4 is over and 3 is under
+    nb = oracle.bias_update(np.zeros(3, np.float32), np.array([4, 3, 3]), T=10, k=1, rate=0.001)
+    assert nb.tolist() == [np.float32(-0.001), np.float32(0.001), np.float32(0.001)]
+    assert nb.dtype == np.float32
+
+
+def test_bias_balancing_evens_a_skewed_router():
+    """[RS] "Keeping the load even", the widget: 256 tokens, 8 experts, a router
+    skewed toward the low-numbered experts; repeated bias steps bring the busiest
+    expert to within a few points of the fair share in 5 to 15 steps and then
+    hover around even."""
+    rng = np.random.default_rng(14)
+    T, E, k = 256, 8, 1
+    s = (rng.normal(size=(T, E)) - 0.3 * np.arange(E)[None, :]).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    shares = []
+    for _ in range(30):
+        idx, _ = oracle.top_k(oracle.selection_keys(s, oracle.SOFTMAX_THEN_TOPK, b), k)
+        counts = np.bincount(idx.ravel(), minlength=E)
+        shares.append(counts.max() / (T * k))
+        b = oracle.bias_update(b, counts, T, k, rate=0.02)
+    assert shares[0] > 0.3                    # skewed before balancing
+    assert min(shares[5:16]) < 0.125 + 0.05   # within a few points by 5 to 15 steps
+    assert max(shares[16:]) < 0.125 + 0.06    # and then it hovers near even
+
+
 def test_active_set_counts(golden):
     g = golden("active_sets.txt")
     assert sum(1 for _ in itertools.combinations(range(16), 2)) == g["c_16_2"]
