@@ -59,7 +59,8 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 
 enum moe_score_mode {
   MOE_SOFTMAX_THEN_TOPK = 0, /* p = softmax over all E scores; weights = p of the chosen k */
-  MOE_TOPK_THEN_SOFTMAX = 1  /* weights = softmax over the chosen k scores */
+  MOE_TOPK_THEN_SOFTMAX = 1, /* weights = softmax over the chosen k scores */
+  MOE_SIGMOID_THEN_TOPK = 2  /* g = sigmoid(score); weights = g of the chosen k over their sum */
 };
 
 #define MOE_MAX_EXPERTS 256
@@ -69,32 +70,59 @@ enum moe_score_mode {
  * moe_route -- router GEMM, top-k selection and gate weights.
  * Sources: Latent "Mixture of experts", "Where the experts live" (s = W_r x and
  * the gate equation); The Residual Stream "Mixture of Experts: More Parameters,
- * Same FLOPs", "The router" (renormalized top-k equation, worked example);
- * Transformers & Math 17.2 (the two softmax orders); ML Interview Notes, the
- * Router listing.
+ * Same FLOPs", "The router" (renormalized top-k equation, worked example;
+ * DeepSeek-V3's sigmoid scores normalized over the chosen experts) and "Keeping
+ * the load even" (bias balancing: a per-expert bias that chooses but never
+ * weights); Transformers & Math 17.2 (the two softmax orders); ML Interview
+ * Notes, the Router listing.
  *
- *   x          device [T][d] dtype        token vectors
- *   w_router   device [E][d] dtype        router weight (nn.Linear(d, E) layout)
- *   logit_bias device [E] float32 or NULL added to every token's scores before
- *                                        selection and softmax
- *   logits     device [T][E] float32 out  s = x W_r^T (+ bias), float32 accumulation
- *                                        (the summation order depends on T: up to
- *                                        2048 bf16 tokens take a split-d kernel;
- *                                        results are deterministic for given T)
- *   topk_idx   device [T][k] int32 out    the k highest scores, best first; equal
- *                                        scores go to the lower expert index
- *   topk_w     device [T][k] float32 out  gate weights by `mode`; with
- *                                        MOE_SOFTMAX_THEN_TOPK and renorm != 0 they
- *                                        are divided by their sum (renorm is
- *                                        ignored for MOE_TOPK_THEN_SOFTMAX)
- *   near_tie   device [T] int32 out       1 where the k-th best score exceeds the
- *                                        (k+1)-th by less than MOE_NEAR_TIE_GAP
- *                                        (0 when k = E)
+ *   x           device [T][d] dtype        token vectors
+ *   w_router    device [E][d] dtype        router weight (nn.Linear(d, E) layout)
+ *   logit_bias  device [E] float32 or NULL added to every token's scores before
+ *                                         selection and softmax
+ *   select_bias device [E] float32 or NULL added only to the selection keys:
+ *                                         softmax(s) + b (MOE_SOFTMAX_THEN_TOPK),
+ *                                         s + b (MOE_TOPK_THEN_SOFTMAX) or
+ *                                         sigmoid(s) + b (MOE_SIGMOID_THEN_TOPK);
+ *                                         never in the weights or the logits.
+ *                                         Without it the key is s, or sigmoid(s).
+ *   logits      device [T][E] float32 out  s = x W_r^T (+ logit_bias), float32
+ *                                         accumulation (the summation order depends
+ *                                         on T: up to 2048 bf16 tokens take a
+ *                                         split-d kernel; results are deterministic
+ *                                         for given T)
+ *   topk_idx    device [T][k] int32 out    the k highest keys, best first; equal
+ *                                         keys go to the lower expert index
+ *   topk_w      device [T][k] float32 out  gate weights by `mode` from the scores;
+ *                                         with MOE_SOFTMAX_THEN_TOPK and renorm != 0
+ *                                         they are divided by their sum (renorm is
+ *                                         ignored by the other two modes; sigmoid
+ *                                         weights are always normalized)
+ *   near_tie    device [T] int32 out       1 where the k-th best key exceeds the
+ *                                         (k+1)-th by less than MOE_NEAR_TIE_GAP
+ *                                         (0 when k = E)
  */
-int moe_route(const void* x, const void* w_router, const float* logit_bias, int dtype,
+int moe_route(const void* x, const void* w_router, const float* logit_bias, const float* select_bias, int dtype,
               int T, int d, int E, int k, int mode, int renorm,
               float* logits, int32_t* topk_idx, float* topk_w, int32_t* near_tie,
               hipStream_t stream);
+
+/*
+ * moe_bias_update -- one step of bias balancing.
+ * Source: The Residual Stream, "Keeping the load even" (after every step, raise
+ * an expert's bias by a fixed amount if it got fewer than its share of tokens,
+ * lower it if it got more) and the MoE listing's update.
+ *
+ *   counts      device [E] int32           demand counts of the step (moe_permute)
+ *   T, k, E                                the step's tokens, slots, experts
+ *   rate        the fixed step
+ *   select_bias device [E] float32 in/out  b_e += rate * sign(T k - E counts_e),
+ *                                         in float32 (the share T k / E is compared
+ *                                         exactly, in integers)
+ * T = 0 leaves the bias unchanged.  A NaN rate returns MOE_ERR_INVALID_ARG.
+ */
+int moe_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* select_bias,
+                    hipStream_t stream);
 
 /*
  * moe_permute -- per-expert histogram, capacity, stable permutation, gather.

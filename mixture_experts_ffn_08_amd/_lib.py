@@ -18,10 +18,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
-MOE_SOFTMAX_THEN_TOPK, MOE_TOPK_THEN_SOFTMAX = 0, 1
+MOE_SOFTMAX_THEN_TOPK, MOE_TOPK_THEN_SOFTMAX, MOE_SIGMOID_THEN_TOPK = 0, 1, 2
 MOE_MAX_EXPERTS = 256
 
-EXPORTS = ("moe_route", "moe_permute", "moe_permute_workspace_bytes", "moe_capacity",
+EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_workspace_bytes", "moe_capacity",
            "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
            "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
 
@@ -30,7 +30,8 @@ _I = ctypes.c_int
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 _SIGS = {
-    "moe_route": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "moe_bias_update": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_capacity": (_I64, [_I64, _I, _I, ctypes.c_double]),
@@ -133,14 +134,21 @@ def moe_stats_workspace_bytes(T: int, E: int) -> int:
 
 
 def moe_route(x, w_router, logit_bias, T, d, E, k, mode, renorm, logits, topk_idx, topk_w, near_tie,
-              stream=None):
+              stream=None, select_bias=None):
     dt = _dtype_code(x)
     args = (_dev(x, "x", x.dtype, T * d), _dev(w_router, "w_router", x.dtype, E * d),
-            _dev(logit_bias, "logit_bias", torch.float32, E, optional=True), dt, T, d, E, k, mode,
+            _dev(logit_bias, "logit_bias", torch.float32, E, optional=True),
+            _dev(select_bias, "select_bias", torch.float32, E, optional=True), dt, T, d, E, k, mode,
             int(bool(renorm)), _dev(logits, "logits", torch.float32, T * E),
             _dev(topk_idx, "topk_idx", torch.int32, T * k), _dev(topk_w, "topk_w", torch.float32, T * k),
             _dev(near_tie, "near_tie", torch.int32, T), _stream(stream))
     _check("moe_route", load().moe_route(*args))
+
+
+def moe_bias_update(counts, T, k, E, rate, select_bias, stream=None):
+    args = (_dev(counts, "counts", torch.int32, E), T, k, E, float(rate),
+            _dev(select_bias, "select_bias", torch.float32, E), _stream(stream))
+    _check("moe_bias_update", load().moe_bias_update(*args))
 
 
 def moe_permute(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm_token, x_perm, workspace,

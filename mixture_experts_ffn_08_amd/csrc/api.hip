@@ -127,17 +127,17 @@ size_t moe_stats_workspace_bytes(int T, int E) {
   return round_up((size_t)moe::stats_blocks(T) * (size_t)E * sizeof(float), 256);
 }
 
-int moe_route(const void* x, const void* w_router, const float* logit_bias, int dtype, int T, int d, int E,
-              int k, int mode, int renorm, float* logits, int32_t* topk_idx, float* topk_w, int32_t* near_tie,
-              hipStream_t stream) {
+int moe_route(const void* x, const void* w_router, const float* logit_bias, const float* select_bias, int dtype,
+              int T, int d, int E, int k, int mode, int renorm, float* logits, int32_t* topk_idx, float* topk_w,
+              int32_t* near_tie, hipStream_t stream) {
   static const char* fn = "moe_route";
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
   if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
-  if (mode != MOE_SOFTMAX_THEN_TOPK && mode != MOE_TOPK_THEN_SOFTMAX)
+  if (mode != MOE_SOFTMAX_THEN_TOPK && mode != MOE_TOPK_THEN_SOFTMAX && mode != MOE_SIGMOID_THEN_TOPK)
     return fail(MOE_ERR_INVALID_ARG, "%s: unknown score mode %d", fn, mode);
   CHECK(experts_check(fn, E, k));
   if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
-  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
+  CHECK(width_check(fn, "d", d, dtype));
   CHECK(assignments_check(fn, T, k));
   if (T == 0) return ok();
   NEED(x, fn);
@@ -146,9 +146,22 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, int 
   NEED(topk_idx, fn);
   NEED(topk_w, fn);
   NEED(near_tie, fn);
-  moe::RouteArgs a{x, w_router, logit_bias, dtype, T, d, E, k, mode, renorm ? 1 : 0,
+  moe::RouteArgs a{x, w_router, logit_bias, select_bias, dtype, T, d, E, k, mode, renorm ? 1 : 0,
                    logits, topk_idx, topk_w, near_tie};
   return hip_status(moe::launch_route(a, stream), fn);
+}
+
+int moe_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* select_bias,
+                    hipStream_t stream) {
+  static const char* fn = "moe_bias_update";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  CHECK(experts_check(fn, E, k));
+  CHECK(assignments_check(fn, T, k));
+  if (!(rate == rate)) return fail(MOE_ERR_INVALID_ARG, "%s: rate is NaN", fn);
+  if (T == 0) return ok();
+  NEED(counts, fn);
+  NEED(select_bias, fn);
+  return hip_status(moe::launch_bias_update(counts, T, k, E, rate, select_bias, stream), fn);
 }
 
 int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,

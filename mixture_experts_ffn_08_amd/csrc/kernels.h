@@ -14,6 +14,7 @@ struct RouteArgs {
   const void* x;
   const void* w_router;
   const float* bias;
+  const float* select_bias;
   int dtype, T, d, E, k, mode, renorm;
   float* logits;
   int32_t* topk_idx;
@@ -21,6 +22,10 @@ struct RouteArgs {
   int32_t* near_tie;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+// b_e += rate * sign(T k - E counts_e) for e < E.
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* bias,
+                              hipStream_t stream);
 
 // Dispatch works on the flattened assignment index p = t*k + j in blocks of
 // kPairsPerBlock assignments.

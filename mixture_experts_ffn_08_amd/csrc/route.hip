@@ -1,10 +1,13 @@
-// Router: scores s = x W_r^T (+ bias), top-k selection and gate weights.
+// Router: scores s = x W_r^T (+ bias), top-k selection and gate weights, with an
+// optional selection-only bias (bias balancing) and sigmoid scoring.
 //
 // Latent "Mixture of experts", "Where the experts live": one score per expert,
 // s = W_r x, and the gate equation (softmax over the chosen scores).
 // The Residual Stream "Mixture of Experts: More Parameters, Same FLOPs", "The
 // router": softmax over all experts, keep the k most probable, renormalize over
-// them.  Transformers & Math 17.2: the two softmax orders.
+// them; DeepSeek-V3's sigmoid scores normalized over the chosen experts.  Same
+// page, "Keeping the load even": a per-expert bias that only chooses.
+// Transformers & Math 17.2: the two softmax orders.
 //
 // Two launch shapes, chosen by T (bf16):
 //  * many tokens: one block of 4 waves takes 64 tokens and every expert (E <= 256,
@@ -61,10 +64,12 @@ __device__ __forceinline__ bool beats(uint32_t ao, uint32_t ai, uint32_t bo, uin
   return ao > bo || (ao == bo && ai < bi);
 }
 
+// One butterfly step of the row arg-max; the winner's value bv travels with it.
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi) {
+__device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi, float& bv) {
   const uint32_t oo = dpp<CTRL>(bo), oi = dpp<CTRL>(bi);
-  if (beats(oo, oi, bo, bi)) { bo = oo; bi = oi; }
+  const float ov = __uint_as_float(dpp<CTRL>(__float_as_uint(bv)));
+  if (beats(oo, oi, bo, bi)) { bo = oo; bi = oi; bv = ov; }
 }
 
 // Top-k for 16 * PASSES tokens of a score tile (LDS, or the score rows in global
@@ -72,12 +77,30 @@ __device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi) {
 // 16 pass + 4 wave + row.  NB keys per lane; SPL result slots per lane (slot j
 // lives in lane j % 16, register j / 16).  WRITE_SCORES copies the tile rows to
 // the score output.
+//
+// Each expert has a base value, which its weight is built from, and a selection
+// key (the base plus the selection bias when there is one):
+//   softmax then top-k:  base e = exp(s - max s); key s, or e / z + b
+//   top-k then softmax:  base s;                  key s, or s + b
+//   sigmoid then top-k:  base g = 1 / (1 + exp(-s)); key g, or g + b
+// The arg-max carries the winner's base; the weights are then e / z (e / sum of
+// the chosen e with renorm), the softmax of the chosen s (an online maximum: with
+// a bias the first winner need not have the largest score), or g / sum of the
+// chosen g.
 template <int NB, int SPL, int PASSES, bool WRITE_SCORES>
 __device__ void select_tile(const float* tile, int stride, int t0, int T, int E, int k, int mode, int renorm,
-                            float* __restrict__ logits, int32_t* __restrict__ topk_idx,
-                            float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
+                            const float* __restrict__ sel_bias, float* __restrict__ logits,
+                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                            int32_t* __restrict__ near_tie) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, row = lane >> 4;
+  const bool biased = sel_bias != nullptr;
+  float sb[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int e = r + 16 * i;
+    sb[i] = biased ? sel_bias[min(e, E - 1)] : 0.f;
+  }
 #pragma unroll 1
   for (int pass = 0; pass < PASSES; ++pass) {
     const int lr = pass * 16 + wave * 4 + row;
@@ -85,39 +108,83 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
     const bool live = t < T;
     const float* s = tile + lr * stride;
     float kf[NB];
-    uint32_t ko[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int e = r + 16 * i;
       const bool present = e < E;
       const float v = (present && live) ? s[e] : 0.f;
       kf[i] = v;
-      ko[i] = present ? max(order_key(v), 1u) : 0u;  // 0 marks "absent or taken"
       if (WRITE_SCORES && present && live) logits[(size_t)t * E + e] = v;
+    }
+    // softmax maximum and denominator over all E
+    float m = 0.f, z = 0.f;
+    float ev[NB];
+    if (mode == MOE_SOFTMAX_THEN_TOPK) {
+      m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (r + 16 * i < E) m = fmaxf(m, kf[i]);
+      m = row16_max(m);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        ev[i] = r + 16 * i < E ? expf(kf[i] - m) : 0.f;
+        z += ev[i];
+      }
+      z = row16_sum(z);
+    }
+    float bv[NB];
+    uint32_t ko[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      float base, key;
+      if (mode == MOE_SOFTMAX_THEN_TOPK) {
+        base = ev[i];
+        key = biased ? ev[i] / z + sb[i] : kf[i];
+      } else if (mode == MOE_TOPK_THEN_SOFTMAX) {
+        base = kf[i];
+        key = biased ? kf[i] + sb[i] : kf[i];
+      } else {
+        base = 1.f / (1.f + expf(-kf[i]));
+        key = biased ? base + sb[i] : base;
+      }
+      bv[i] = base;
+      ko[i] = r + 16 * i < E ? max(order_key(key), 1u) : 0u;  // 0 marks "absent or taken"
     }
     const int rounds = k < E ? k + 1 : k;
     uint32_t my_idx[SPL];
-    float my_key[SPL];
+    float my_val[SPL];
 #pragma unroll
-    for (int q = 0; q < SPL; ++q) { my_idx[q] = 0u; my_key[q] = 0.f; }
-    float top = 0.f, kth = 0.f, next = 0.f, ssum = 0.f;
+    for (int q = 0; q < SPL; ++q) { my_idx[q] = 0u; my_val[q] = 0.f; }
+    float kth = 0.f, next = 0.f, vsum = 0.f, vmax = 0.f;
     for (int j = 0; j < rounds; ++j) {
       uint32_t bo = 0u, bi = 0xffffffffu;
+      float bval = 0.f;
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        if (ko[i] > bo) { bo = ko[i]; bi = r + 16 * i; }  // strict: the lower index keeps a tie
-      argmax_step<kDppXor1>(bo, bi);
-      argmax_step<kDppXor2>(bo, bi);
-      argmax_step<kDppHalfMirror>(bo, bi);
-      argmax_step<kDppMirror>(bo, bi);
+        if (ko[i] > bo) { bo = ko[i]; bi = r + 16 * i; bval = bv[i]; }  // strict: the lower index keeps a tie
+      argmax_step<kDppXor1>(bo, bi, bval);
+      argmax_step<kDppXor2>(bo, bi, bval);
+      argmax_step<kDppHalfMirror>(bo, bi, bval);
+      argmax_step<kDppMirror>(bo, bi, bval);
       const float wkey = key_value(bo);
-      if (j == 0) top = wkey;
       if (j < k) {
         if (j == k - 1) kth = wkey;
-        ssum += expf(wkey - top);
+        if (mode == MOE_TOPK_THEN_SOFTMAX) {  // running softmax over the chosen scores
+          if (j == 0) {
+            vmax = bval;
+            vsum = 1.f;
+          } else if (bval > vmax) {
+            vsum = vsum * expf(vmax - bval) + 1.f;
+            vmax = bval;
+          } else {
+            vsum += expf(bval - vmax);
+          }
+        } else {
+          vsum += bval;
+        }
 #pragma unroll
         for (int q = 0; q < SPL; ++q)
-          if (j == r + 16 * q) { my_idx[q] = bi; my_key[q] = wkey; }
+          if (j == r + 16 * q) { my_idx[q] = bi; my_val[q] = bval; }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
           if (bi == (uint32_t)(r + 16 * i)) ko[i] = 0u;
@@ -125,19 +192,17 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
         next = wkey;
       }
     }
-    float z = 0.f;
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      if (r + 16 * i < E) z += expf(kf[i] - top);
-    z = row16_sum(z);
-    const float denom = (mode == MOE_TOPK_THEN_SOFTMAX || renorm) ? ssum : z;
     if (live) {
 #pragma unroll
       for (int q = 0; q < SPL; ++q) {
         const int j = r + 16 * q;
         if (j < k) {
+          float w;
+          if (mode == MOE_SOFTMAX_THEN_TOPK) w = my_val[q] / (renorm ? vsum : z);
+          else if (mode == MOE_TOPK_THEN_SOFTMAX) w = expf(my_val[q] - vmax) / vsum;
+          else w = my_val[q] / vsum;
           topk_idx[(size_t)t * k + j] = (int32_t)my_idx[q];
-          topk_w[(size_t)t * k + j] = expf(my_key[q] - top) / denom;
+          topk_w[(size_t)t * k + j] = w;
         }
       }
       if (r == 0) near_tie[t] = (k < E && ((double)kth - (double)next) < MOE_NEAR_TIE_GAP) ? 1 : 0;
@@ -148,7 +213,7 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
 template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    int T, int d, int E, int k, int mode, int renorm, float* __restrict__ logits,
+    const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm, float* __restrict__ logits,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
   using L = RouteLds<NB>;
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
@@ -229,8 +294,8 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     for (int i = 0; i < 4; ++i) tile[(wave * 16 + 4 * kg + i) * L::kTileStride + n] = acc[nb][i] + b;
   }
   __syncthreads();
-  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w,
-                                near_tie);
+  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx,
+                                topk_w, near_tie);
 }
 
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
@@ -292,19 +357,21 @@ __global__ __launch_bounds__(kSplitWaves * 64) void route_scores_split_kernel(
 // Selection from the score rows written by route_scores_split_kernel.
 template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_select_kernel(int T, int E, int k, int mode, int renorm,
+                                                           const float* __restrict__ sel_bias,
                                                            const float* __restrict__ scores,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w,
                                                            int32_t* __restrict__ near_tie) {
   const int t0 = blockIdx.x * kSelectTokens;
-  select_tile<NB, SPL, kSelectTokens / 16, false>(scores + (size_t)t0 * E, E, t0, T, E, k, mode, renorm, nullptr,
-                                                  topk_idx, topk_w, near_tie);
+  select_tile<NB, SPL, kSelectTokens / 16, false>(scores + (size_t)t0 * E, E, t0, T, E, k, mode, renorm, sel_bias,
+                                                  nullptr, topk_idx, topk_w, near_tie);
 }
 
 template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_f32_kernel(
-    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias, int T,
-    int d, int E, int k, int mode, int renorm, float* __restrict__ logits, int32_t* __restrict__ topk_idx,
+    const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
+    const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
   using L = RouteLds<NB>;
   __shared__ __attribute__((aligned(16))) float tile[kTokens * L::kTileStride];
@@ -323,8 +390,8 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     tile[lr * L::kTileStride + n] = acc;
   }
   __syncthreads();
-  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, logits, topk_idx, topk_w,
-                                near_tie);
+  select_tile<NB, SPL, 4, true>(tile, L::kTileStride, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx,
+                                topk_w, near_tie);
 }
 
 template <int NB, int SPL>
@@ -335,15 +402,16 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(route_scores_split_kernel, sgrid, dim3(kSplitWaves * 64), 0, stream,
                        (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.logits);
     hipLaunchKernelGGL((route_select_kernel<NB, SPL>), dim3((a.T + kSelectTokens - 1) / kSelectTokens), block, 0,
-                       stream, a.T, a.E, a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
+                       stream, a.T, a.E, a.k, a.mode, a.renorm, a.select_bias, a.logits, a.topk_idx, a.topk_w,
+                       a.near_tie);
   } else if (a.dtype == MOE_BF16)
     hipLaunchKernelGGL((route_bf16_kernel<NB, SPL>), grid, block, 0, stream, (const uint16_t*)a.x,
-                       (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
-                       a.topk_idx, a.topk_w, a.near_tie);
+                       (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
+                       a.logits, a.topk_idx, a.topk_w, a.near_tie);
   else
     hipLaunchKernelGGL((route_f32_kernel<NB, SPL>), grid, block, 0, stream, (const float*)a.x,
-                       (const float*)a.w_router, a.bias, a.T, a.d, a.E, a.k, a.mode, a.renorm, a.logits,
-                       a.topk_idx, a.topk_w, a.near_tie);
+                       (const float*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
+                       a.logits, a.topk_idx, a.topk_w, a.near_tie);
   return hipGetLastError();
 }
 

@@ -169,7 +169,27 @@ __global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restr
   finish_stats(sum, counts, T, k, E, alpha, f, P, l_aux, max_over_mean);
 }
 
+// Bias balancing (The Residual Stream, "Keeping the load even", and the MoE
+// listing's step after each batch): raise b_e by `rate` when expert e got fewer
+// than its share of the T k assignments, lower it when it got more.  The share is
+// compared exactly, as integers: T k against E counts_e.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts, int64_t tk, int E,
+                                                           float rate, float* __restrict__ bias) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  const int64_t diff = tk - (int64_t)E * counts[e];
+  const float sign = diff > 0 ? 1.f : (diff < 0 ? -1.f : 0.f);
+  bias[e] = bias[e] + rate * sign;  // rate * sign is exact: one rounding, as in float32 arithmetic
+}
+
 }  // namespace
+
+hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* bias,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, counts, (int64_t)T * k, E,
+                     rate, bias);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream) {
   const int nblk = stats_blocks(a.T);

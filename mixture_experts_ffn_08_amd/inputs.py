@@ -44,9 +44,10 @@ import numpy as np
 # Score modes, numbered as in include/moe.h.
 SOFTMAX_THEN_TOPK = 0
 TOPK_THEN_SOFTMAX = 1
+SIGMOID_THEN_TOPK = 2
 
 # Stream keys.
-_X, _W_ROUTER, _BIAS_PERM, _EXPERT, _SHARED = 0, 1, 2, 3, 4
+_X, _W_ROUTER, _BIAS_PERM, _EXPERT, _SHARED, _SELECT_BIAS = 0, 1, 2, 3, 4, 5
 _GATE, _UP, _DOWN = 0, 1, 2
 
 
@@ -57,10 +58,13 @@ class LayerShape:
     dtype   "f32" or "bf16": storage type of x, all weights, activations and y.
     T       tokens; d model width; E routed experts; k experts per token;
     F       routed expert hidden width; F_shared shared expert width (0 = none).
-    mode    SOFTMAX_THEN_TOPK or TOPK_THEN_SOFTMAX; renorm applies to the former.
+    mode    SOFTMAX_THEN_TOPK, TOPK_THEN_SOFTMAX or SIGMOID_THEN_TOPK; renorm
+            applies to the first.
     phi     capacity factor, or None for dropless routing.
     zipf_bias  add the skewed per-expert logit bias described above.
     alpha   weight of the balance term.
+    select_bias  standard deviation of a seeded per-expert selection-only bias
+            (normal, float32); 0 = none.
     """
 
     name: str
@@ -76,6 +80,7 @@ class LayerShape:
     phi: Optional[float]
     zipf_bias: bool
     alpha: float = 0.01
+    select_bias: float = 0.0
 
     def with_(self, **kw) -> "LayerShape":
         return dataclasses.replace(self, **kw)
@@ -149,6 +154,9 @@ class LayerInputs:
         self.x = _normal(seed, (_X,), (s.T, s.d), 1, s.dtype)
         self.w_router = _normal(seed, (_W_ROUTER,), (s.E, s.d), s.d, s.dtype)
         self.bias = zipf_logit_bias(s.E, seed) if s.zipf_bias else None
+        self.select_bias = (None if s.select_bias == 0 else
+                            (_rng(seed, _SELECT_BIAS).standard_normal(s.E, dtype=np.float32) *
+                             np.float32(s.select_bias)).astype(np.float32))
 
     def expert(self, e: int):
         """(gate[F][d], up[F][d], down[d][F]) of routed expert e."""

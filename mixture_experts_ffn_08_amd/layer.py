@@ -41,6 +41,9 @@ class DeviceWeights:
         td = torch_dtype(s.dtype)
         self.w_router = to_device(inputs.w_router, s.dtype, self.device)
         self.bias = None if inputs.bias is None else torch.from_numpy(inputs.bias).to(self.device)
+        # selection-only bias (bias balancing): updated in place by MoeLayer.bias_update
+        self.select_bias = (None if inputs.select_bias is None else
+                            torch.from_numpy(inputs.select_bias.copy()).to(self.device))
         self.gate = torch.empty((s.E, s.F, s.d), dtype=td, device=self.device)
         self.up = torch.empty((s.E, s.F, s.d), dtype=td, device=self.device)
         self.down = torch.empty((s.E, s.d, s.F), dtype=td, device=self.device)
@@ -109,7 +112,14 @@ class MoeLayer:
     def route(self, x, b: Buffers, stream=None):
         s = self.shape
         _lib.moe_route(x, self.w.w_router, self.w.bias, b.T, s.d, s.E, s.k, s.mode, s.renorm, b.logits,
-                       b.topk_idx, b.topk_w, b.near_tie, stream)
+                       b.topk_idx, b.topk_w, b.near_tie, stream, select_bias=self.w.select_bias)
+
+    def bias_update(self, b: Buffers, rate: float, stream=None):
+        """One bias-balancing step from the demand counts of the last permute."""
+        s = self.shape
+        if self.w.select_bias is None:
+            raise ValueError("this layer has no selection bias")
+        _lib.moe_bias_update(b.counts, b.T, s.k, s.E, rate, self.w.select_bias, stream)
 
     def permute(self, x, b: Buffers, stream=None):
         """Dispatch; also gathers x_perm when the buffers hold one."""

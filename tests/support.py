@@ -76,38 +76,44 @@ class GpuRun:
         torch.cuda.empty_cache()
 
 
-def oracle_route(inp):
+def oracle_route(inp, select_bias=None):
     s = inp.shape
+    sb = inp.select_bias if select_bias is None else select_bias
     return oracle.route(minp.as_f32(inp.x, s.dtype), minp.as_f32(inp.w_router, s.dtype), inp.bias, s.k, s.mode,
-                        s.renorm)
+                        s.renorm, sb)
 
 
-def check_route(inp, out, ref=None):
-    """Scores within fp32 tolerance.  Outside near-tie tokens (k-th and (k+1)-th
-    scores closer than the gap, on either side) the chosen expert set is exact;
-    the slot order is exact where consecutive chosen scores are farther apart
-    than the gap, and elsewhere follows the kernel's own scores (descending);
-    gate weights, matched by expert, within tolerance.  Returns the tokens whose
-    chosen set may differ."""
+def check_route(inp, out, ref=None, select_bias=None):
+    """Scores within fp32 tolerance.  Selection runs on keys (the scores, their
+    sigmoid, or with a selection bias softmax/score/sigmoid + b).  Outside
+    near-tie tokens (k-th and (k+1)-th keys closer than the gap, on either side)
+    the chosen expert set is exact; the slot order is exact where consecutive
+    chosen keys are farther apart than the gap, and elsewhere follows the
+    kernel's own keys (descending, up to their rounding); gate weights, matched by
+    expert, within tolerance.  Returns the tokens whose chosen set may differ."""
     s = inp.shape
-    scores, idx, w, near = ref if ref is not None else oracle_route(inp)
+    sb = inp.select_bias if select_bias is None else select_bias
+    scores, idx, w, near = ref if ref is not None else oracle_route(inp, sb)
     smax = np.abs(scores).max()
     assert np.abs(out["scores"] - scores).max() <= 1e-4 * smax + 1e-6
     tie = (near == 1) | (out["near_tie"] == 1)
     ok = ~tie
     assert np.array_equal(np.sort(out["idx"][ok], 1), np.sort(idx[ok], 1)), "expert sets differ outside near ties"
-    top = -np.sort(-scores.astype(np.float64), axis=1)[:, :s.k]
+    keys = oracle.selection_keys(scores, s.mode, sb).astype(np.float64)
+    top = -np.sort(-keys, axis=1)[:, :s.k]
     order_tie = (top[:, :-1] - top[:, 1:] < oracle.NEAR_TIE_GAP).any(1)
     strict = ok & ~order_tie
-    assert np.array_equal(out["idx"][strict], idx[strict]), "slot order differs where the scores are well apart"
-    own = np.take_along_axis(out["scores"], out["idx"].astype(np.int64), 1)
-    assert np.all(own[:, :-1] >= own[:, 1:]), "slots not in descending order of the kernel's scores"
+    assert np.array_equal(out["idx"][strict], idx[strict]), "slot order differs where the keys are well apart"
+    own_keys = oracle.selection_keys(out["scores"], s.mode, sb).astype(np.float64)
+    own = np.take_along_axis(own_keys, out["idx"].astype(np.int64), 1)
+    slack = 0.0 if (sb is None and s.mode != oracle.SIGMOID_THEN_TOPK) else 1e-6
+    assert np.all(own[:, :-1] >= own[:, 1:] - slack), "slots not in descending order of the kernel's keys"
     by_expert = lambda a, i: np.take_along_axis(a, np.argsort(i, 1), 1)
     np.testing.assert_allclose(by_expert(out["w"][ok], out["idx"][ok]), by_expert(w[ok], idx[ok]),
                                rtol=W_RTOL, atol=W_ATOL)
     # near-tie flags only differ where the oracle's gap sits at the threshold
     if s.k < s.E:
-        srt = -np.sort(-scores.astype(np.float64), axis=1)
+        srt = -np.sort(-keys, axis=1)
         gap = srt[:, s.k - 1] - srt[:, s.k]
         diff = out["near_tie"] != near
         assert np.all(np.abs(gap[diff] - oracle.NEAR_TIE_GAP) < 1e-5)

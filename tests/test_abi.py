@@ -65,22 +65,34 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 
 
 def route(**kw):
-    a = dict(x=FAKE, w=FAKE, bias=None, dtype=1, T=4, d=128, E=8, k=2, mode=0, renorm=1, logits=FAKE,
+    a = dict(x=FAKE, w=FAKE, bias=None, sel=None, dtype=1, T=4, d=128, E=8, k=2, mode=0, renorm=1, logits=FAKE,
              idx=FAKE, w_out=FAKE, near=FAKE)
     a.update(kw)
-    return _lib.load().moe_route(a["x"], a["w"], a["bias"], a["dtype"], a["T"], a["d"], a["E"], a["k"],
+    return _lib.load().moe_route(a["x"], a["w"], a["bias"], a["sel"], a["dtype"], a["T"], a["d"], a["E"], a["k"],
                                  a["mode"], a["renorm"], a["logits"], a["idx"], a["w_out"], a["near"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(T=-1), -1), (dict(dtype=7), -1), (dict(mode=2), -1), (dict(E=0), -1), (dict(E=257), -2),
-    (dict(k=0), -1), (dict(k=9), -1), (dict(d=0), -1), (dict(d=12), -2), (dict(x=None), -1),
-    (dict(w=None), -1), (dict(logits=None), -1), (dict(idx=None), -1), (dict(w_out=None), -1),
-    (dict(near=None), -1), (dict(T=2 ** 30, k=4), -2),
+    (dict(T=-1), -1), (dict(dtype=7), -1), (dict(mode=3), -1), (dict(mode=-1), -1), (dict(E=0), -1),
+    (dict(E=257), -2), (dict(k=0), -1), (dict(k=9), -1), (dict(d=0), -1), (dict(d=136), -2),
+    (dict(dtype=0, d=12), -2), (dict(x=None), -1), (dict(w=None), -1), (dict(logits=None), -1),
+    (dict(idx=None), -1), (dict(w_out=None), -1), (dict(near=None), -1), (dict(T=2 ** 30, k=4), -2),
+    (dict(mode=2, x=None), -1), (dict(mode=2, sel=FAKE, near=None), -1),
 ])
 def test_route_rejects_before_launch(kw, status):
     assert route(**kw) == status
     assert _lib.last_error()
+
+
+def test_bias_update_rejects_before_launch():
+    lib = _lib.load()
+    assert lib.moe_bias_update(FAKE, -1, 2, 8, 0.01, FAKE, None) == -1
+    assert lib.moe_bias_update(FAKE, 4, 9, 8, 0.01, FAKE, None) == -1
+    assert lib.moe_bias_update(FAKE, 4, 2, 300, 0.01, FAKE, None) == -2
+    assert lib.moe_bias_update(None, 4, 2, 8, 0.01, FAKE, None) == -1
+    assert lib.moe_bias_update(FAKE, 4, 2, 8, 0.01, None, None) == -1
+    assert lib.moe_bias_update(FAKE, 4, 2, 8, float("nan"), FAKE, None) == -1
+    assert lib.moe_bias_update(None, 0, 2, 8, 0.01, None, None) == 0  # no tokens: nothing to do
 
 
 def test_route_zero_tokens_is_a_no_op():
