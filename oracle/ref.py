@@ -250,6 +250,43 @@ def dispatch(idx: np.ndarray, E: int, cap: Optional[int]):
             row_of.astype(np.int32), perm_token.astype(np.int32))
 
 
+def dispatch_padded(idx: np.ndarray, E: int, cap: int):
+    """The same dispatch in a capacity-padded layout: every expert owns C = cap
+    slots, expert e's r-th kept assignment sits in slot e C + r, and the slots
+    past its kept count are padding ([TM] 17.5: each expert processes at most C
+    tokens in a fixed-size buffer; [UD] "Capacity"; [RS] "What experts cost at
+    serving time": the buffers an expert-parallel exchange sends).
+
+    Returns counts[E] (demand), offsets[E+1] = e C, row_of[T][k] (slot, -1 when
+    dropped) and slot_token[E C] (token of each slot, -1 for padding)."""
+    if cap is None or cap < 1:
+        raise ValueError("the padded layout needs a capacity of at least 1")
+    counts, offsets, row_of, perm_token = dispatch(idx, E, cap)
+    kept = np.diff(offsets).astype(np.int64)
+    slot_token = np.full(E * cap, -1, np.int64)
+    row_pad = np.full(row_of.shape, -1, np.int64)
+    for e in range(E):
+        for r in range(int(kept[e])):
+            slot_token[e * cap + r] = perm_token[offsets[e] + r]
+    for t in range(row_of.shape[0]):
+        for j in range(row_of.shape[1]):
+            r = int(row_of[t, j])
+            if r >= 0:
+                e = int(idx[t, j])
+                row_pad[t, j] = e * cap + (r - int(offsets[e]))
+    return (counts, (np.arange(E + 1, dtype=np.int64) * cap).astype(np.int32),
+            row_pad.astype(np.int32), slot_token.astype(np.int32))
+
+
+def gather_slots(x: np.ndarray, slot_token: np.ndarray) -> np.ndarray:
+    """x_slots[s] = x[slot_token[s]], zeros for padding slots (token -1)."""
+    x = np.asarray(x)
+    st = np.asarray(slot_token, np.int64)
+    out = np.zeros((st.shape[0], x.shape[1]), x.dtype)
+    out[st >= 0] = x[st[st >= 0]]
+    return out
+
+
 def permute_rows(x: np.ndarray, perm_token: np.ndarray) -> np.ndarray:
     """x_perm[r] = x[perm_token[r]] ([MIN] x_flat[tok]; [RS] x[rows])."""
     return np.asarray(x)[np.asarray(perm_token, np.int64)]

@@ -268,6 +268,35 @@ def test_dispatch_brute_force(T, E, k, phi):
                 assert row_of[t, j] == -1
 
 
+@pytest.mark.parametrize("T,E,k,phi", [(40, 4, 1, 0.5), (37, 6, 2, 1.0), (50, 8, 3, 1.25), (23, 5, 5, 0.7)])
+def test_dispatch_padded_brute_force(T, E, k, phi):
+    """Slot e C + rank for the kept assignments (rank by definition: earlier
+    tokens that chose the same expert), -1 padding elsewhere; the gathered slots
+    hold the token rows and zeros."""
+    rng = np.random.default_rng(T * E + k)
+    idx = _random_routing(rng, T, E, k, skew=1.5)
+    C = oracle.capacity(T, k, E, phi)
+    counts, offsets, row_of, slot_token = oracle.dispatch_padded(idx, E, C)
+    rank = _rank_by_definition(idx)
+    assert offsets.tolist() == [e * C for e in range(E + 1)]
+    expect = np.full(E * C, -1)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            if rank[t, j] < C:
+                assert row_of[t, j] == e * C + rank[t, j]
+                expect[e * C + rank[t, j]] = t
+            else:
+                assert row_of[t, j] == -1
+    assert slot_token.tolist() == expect.tolist()
+    for e in range(E):
+        assert counts[e] == int((idx == e).sum())
+    x = rng.normal(size=(T, 3))
+    xs = oracle.gather_slots(x, slot_token)
+    for sl in range(E * C):
+        assert np.array_equal(xs[sl], x[slot_token[sl]] if slot_token[sl] >= 0 else np.zeros(3))
+
+
 def test_dispatch_invariants():
     rng = np.random.default_rng(5)
     T, E, k = 300, 16, 4
