@@ -155,6 +155,30 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity,
                 int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token,
                 void* x_perm, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * moe_permute_padded -- the same dispatch in a capacity-padded layout: each
+ * expert owns `capacity` (C) slots, as in the fixed-size buffers an
+ * expert-parallel exchange sends.
+ * Sources: Transformers & Math 17.5 (each expert processes at most C tokens);
+ * Understanding Data, "The maths", "Capacity"; The Residual Stream, "What
+ * experts cost at serving time" (experts spread over devices).
+ *
+ * Arguments as moe_permute, except:
+ *   capacity   C >= 1 (required); E * C <= 2^31 - 1
+ *   offsets    device [E+1] int32 out    e * C (the group bounds for the grouped
+ *                                        GEMMs over all E * C slots)
+ *   row_of     device [T][k] int32 out   slot e * C + rank of the assignment,
+ *                                        -1 when dropped
+ *   slot_token device [E*C] int32 out    token of each slot; -1 for the slots past
+ *                                        an expert's kept count min(counts_e, C)
+ *   x_slots    device [E*C][d] or NULL   x[slot_token[s]], zero rows for padding
+ * Padding slots take part in the grouped GEMMs (their outputs are computed and
+ * never read by moe_combine).
+ */
+int moe_permute_padded(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
+                       int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* slot_token,
+                       void* x_slots, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 size_t moe_permute_workspace_bytes(int T, int k, int E);
 
 /*
@@ -224,13 +248,15 @@ int moe_grouped_swiglu(const void* x, const int32_t* row_index, int src_rows,
  * expert(x)); Transformers & Math 17.5 (a dropped slot adds nothing and the
  * other weights are kept as they are).
  * The sum runs in slot order in float32 and is rounded once: the result is
- * deterministic.  row_of values outside [0, T*k) count as dropped.
+ * deterministic.  row_of values outside [0, y_rows) count as dropped.
  *
- *   y_perm   device [T*k][d] dtype; row_of device [T][k] int32;
- *   topk_w   device [T][k] float32; shared_y device [T][d] dtype or NULL;
+ *   y_perm   device [y_rows][d] dtype: T*k rows for the compact layout
+ *            (moe_permute), E*C for the padded one (moe_permute_padded)
+ *   row_of   device [T][k] int32; topk_w device [T][k] float32;
+ *   shared_y device [T][d] dtype or NULL;
  *   y        device [T][d] dtype out (every row written)
  */
-int moe_combine(const void* y_perm, const int32_t* row_of, const float* topk_w,
+int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const float* topk_w,
                 const void* shared_y, int dtype, int T, int k, int d, void* y,
                 hipStream_t stream);
 

@@ -21,7 +21,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_THEN_TOPK, MOE_TOPK_THEN_SOFTMAX, MOE_SIGMOID_THEN_TOPK = 0, 1, 2
 MOE_MAX_EXPERTS = 256
 
-EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_workspace_bytes", "moe_capacity",
+EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_padded", "moe_permute_workspace_bytes", "moe_capacity",
            "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
            "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
 
@@ -33,12 +33,13 @@ _SIGS = {
     "moe_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_bias_update": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_padded": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_capacity": (_I64, [_I64, _I, _I, ctypes.c_double]),
     "moe_grouped_gate_up": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _I, _P, _P]),
     "moe_grouped_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "moe_grouped_swiglu": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P]),
-    "moe_combine": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_stats": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_stats_workspace_bytes": (_SZ, [_I, _I]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -165,6 +166,21 @@ def moe_permute(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm
     _check("moe_permute", load().moe_permute(*args))
 
 
+def moe_permute_padded(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, slot_token, x_slots,
+                       workspace, stream=None):
+    """Capacity-padded layout: slot_token and x_slots hold E * capacity slots."""
+    dt = _dtype_code(x)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    slots = E * int(capacity)
+    args = (_dev(topk_idx, "topk_idx", torch.int32, T * k), T, k, E, int(capacity),
+            _dev(x, "x", x.dtype, T * d), dt, d, _dev(counts, "counts", torch.int32, E),
+            _dev(offsets, "offsets", torch.int32, E + 1), _dev(row_of, "row_of", torch.int32, T * k),
+            _dev(slot_token, "slot_token", torch.int32, slots),
+            _dev(x_slots, "x_slots", x.dtype, slots * d, optional=True),
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("moe_permute_padded", load().moe_permute_padded(*args))
+
+
 def _rows_args(x, row_index, src_rows, max_rows, d):
     if row_index is None:
         return _dev(x, "x", x.dtype, max_rows * d), 0, 0
@@ -201,9 +217,11 @@ def moe_grouped_swiglu(x, row_index, src_rows, offsets, G, max_rows, d, F, w_gat
     _check("moe_grouped_swiglu", load().moe_grouped_swiglu(*args))
 
 
-def moe_combine(y_perm, row_of, topk_w, shared_y, T, k, d, y, stream=None):
+def moe_combine(y_perm, row_of, topk_w, shared_y, T, k, d, y, stream=None, y_rows=None):
+    """y_rows: rows of y_perm (default T*k, the compact layout; E*C for the padded one)."""
     dt = _dtype_code(y)
-    args = (_dev(y_perm, "y_perm", y.dtype, T * k * d), _dev(row_of, "row_of", torch.int32, T * k),
+    rows = T * k if y_rows is None else int(y_rows)
+    args = (_dev(y_perm, "y_perm", y.dtype, rows * d), rows, _dev(row_of, "row_of", torch.int32, T * k),
             _dev(topk_w, "topk_w", torch.float32, T * k),
             _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), dt, T, k, d,
             _dev(y, "y", y.dtype, T * d), _stream(stream))

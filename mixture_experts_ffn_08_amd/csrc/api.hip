@@ -188,7 +188,39 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, 
   const size_t half = need / 2;
   moe::PermuteArgs a{topk_idx, T, k, E, capacity < 0 ? -1 : capacity, x, d * elem_bytes(dtype), counts,
                      offsets, row_of, perm_token, x_perm, static_cast<int32_t*>(workspace),
-                     reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half)};
+                     reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half), 0};
+  return hip_status(moe::launch_permute(a, stream), fn);
+}
+
+int moe_permute_padded(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
+                       int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* slot_token,
+                       void* x_slots, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "moe_permute_padded";
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
+  CHECK(experts_check(fn, E, k));
+  if (capacity < 1) return fail(MOE_ERR_INVALID_ARG, "%s: capacity = %lld must be at least 1", fn,
+                                (long long)capacity);
+  if ((int64_t)E * capacity > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: E*capacity = %lld exceeds 2^31-1", fn, (long long)((int64_t)E * capacity));
+  if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
+  if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
+  CHECK(assignments_check(fn, T, k));
+  if (T == 0) return ok();
+  NEED(topk_idx, fn);
+  NEED(counts, fn);
+  NEED(offsets, fn);
+  NEED(row_of, fn);
+  NEED(slot_token, fn);
+  if (x_slots != nullptr) NEED(x, fn);
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  const size_t half = need / 2;
+  moe::PermuteArgs a{topk_idx, T, k, E, capacity, x, d * elem_bytes(dtype), counts, offsets, row_of, slot_token,
+                     x_slots, static_cast<int32_t*>(workspace),
+                     reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half), 1};
   return hip_status(moe::launch_permute(a, stream), fn);
 }
 
@@ -254,10 +286,11 @@ int moe_grouped_swiglu(const void* x, const int32_t* row_index, int src_rows, co
   return moe_grouped_down(a, offsets, G, max_rows, F, d, w_down, dtype, y_perm, stream);
 }
 
-int moe_combine(const void* y_perm, const int32_t* row_of, const float* topk_w, const void* shared_y,
+int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const float* topk_w, const void* shared_y,
                 int dtype, int T, int k, int d, void* y, hipStream_t stream) {
   static const char* fn = "moe_combine";
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (y_rows < 0) return fail(MOE_ERR_INVALID_ARG, "%s: y_rows = %d < 0", fn, y_rows);
   if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
   if (k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: k = %d < 1", fn, k);
   if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
@@ -268,7 +301,7 @@ int moe_combine(const void* y_perm, const int32_t* row_of, const float* topk_w, 
   NEED(row_of, fn);
   NEED(topk_w, fn);
   NEED(y, fn);
-  moe::CombineArgs c{y_perm, row_of, topk_w, shared_y, dtype, T, k, d, y};
+  moe::CombineArgs c{y_perm, row_of, topk_w, shared_y, dtype, T, k, d, y_rows, y};
   return hip_status(moe::launch_combine(c, stream), fn);
 }
 

@@ -40,22 +40,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                        const int32_t* __restrict__ row_of,
                                                        const float* __restrict__ topk_w,
                                                        const void* __restrict__ shared_y, int T, int k_rt, int d,
-                                                       void* __restrict__ y) {
+                                                       int y_rows, void* __restrict__ y) {
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int k = KT > 0 ? KT : k_rt;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   const int chunks = d / EPC;
-  const int64_t rows = (int64_t)T * k;
+  const int64_t rows = y_rows;
   const size_t row_bytes = (size_t)d * (BF16 ? 2 : 4);
   const char* yp = static_cast<const char*>(y_perm);
   const char* sh = static_cast<const char*>(shared_y);
   char* yt = static_cast<char*>(y) + (size_t)t * row_bytes;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if constexpr (KT > 0) {
-    // A dropped slot reads row 0 (y_perm has T k >= 1 rows) and its values are
-    // replaced by zeros after the load: no load sits under a branch.
+    // A dropped slot reads row 0 (y_perm has y_rows >= 1 rows when any slot is
+    // kept) and its values are replaced by zeros after the load: no load sits
+    // under a branch.
     const char* src[KT];
     float w[KT];
     bool kept[KT];
@@ -127,10 +128,10 @@ hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
   do {                                                                                                        \
     if (a.shared_y != nullptr)                                                                                \
       hipLaunchKernelGGL((combine_kernel<BF16, KT, true>), grid, block, 0, stream, a.y_perm, a.row_of,      \
-                         a.topk_w, a.shared_y, a.T, a.k, a.d, a.y);                                           \
+                         a.topk_w, a.shared_y, a.T, a.k, a.d, a.y_rows, a.y);                                 \
     else                                                                                                      \
       hipLaunchKernelGGL((combine_kernel<BF16, KT, false>), grid, block, 0, stream, a.y_perm, a.row_of,     \
-                         a.topk_w, nullptr, a.T, a.k, a.d, a.y);                                              \
+                         a.topk_w, nullptr, a.T, a.k, a.d, a.y_rows, a.y);                                    \
   } while (0)
   switch (a.k) {
     case 1: MOE_COMBINE(1); break;

@@ -45,6 +45,7 @@ struct PermuteArgs {
   void* x_perm;
   int32_t* block_counts;  // workspace [nblk][E]
   int32_t* block_base;    // workspace [nblk][E]
+  int padded;             // 1: slot e * capacity + rank, offsets e * capacity, padding -1 / zero rows
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 
@@ -70,6 +71,7 @@ struct CombineArgs {
   const float* topk_w;
   const void* shared_y;
   int dtype, T, k, d;
+  int y_rows;  // rows of y_perm; row_of values outside [0, y_rows) count as dropped
   void* y;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kBP) void hist_kernel(const int32_t* __restrict__ i
 // running base of its blocks; the kept counts are then scanned over experts in
 // LDS for the offsets.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
-                                                     int E, int tpe, int64_t cap,
+                                                     int E, int tpe, int64_t cap, int padded,
                                                      int32_t* __restrict__ block_base,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets) {
@@ -99,13 +99,26 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     __syncthreads();
     src ^= 1;
   }
-  if (tid < E) offsets[tid + 1] = kept_s[src][tid];
-  if (tid == 0) offsets[0] = 0;
+  if (!padded) {
+    if (tid < E) offsets[tid + 1] = kept_s[src][tid];
+    if (tid == 0) offsets[0] = 0;
+  }
+}
+
+// Padded layout: offsets[e] = e C, and every slot past its expert's kept count
+// marked -1 (the rank kernels fill the kept slots; the two write disjoint slots).
+__global__ __launch_bounds__(256) void pad_kernel(const int32_t* __restrict__ counts, int E, int cap,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ slot_token) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s <= E) offsets[s] = (int32_t)(s * cap);
+  if (s >= (int64_t)E * cap) return;
+  const int e = (int)(s / cap), r = (int)(s % cap);
+  if (r >= min(counts[e], cap)) slot_token[s] = -1;
 }
 
 __global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ idx, int64_t P, int k, int E,
                                                     int64_t cap, const int32_t* __restrict__ block_base,
-                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ offsets, int padded,
                                                     int32_t* __restrict__ row_of,
                                                     int32_t* __restrict__ perm_token) {
   __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
@@ -127,7 +140,7 @@ __global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ i
     for (int q = 0; q < w; ++q) r += __popc(m[q]);
     const int rank = block_base[(size_t)blockIdx.x * E + e] + r;
     if (cap < 0 || rank < cap) {
-      row = offsets[e] + rank;
+      row = padded ? (int)(e * cap) + rank : offsets[e] + rank;
       perm_token[row] = (int32_t)(p / k);
     }
   }
@@ -137,14 +150,21 @@ __global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ i
 __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
                                                       const int32_t* __restrict__ perm_token,
                                                       const int32_t* __restrict__ offsets_end, int T,
-                                                      int max_rows, int row_bytes, char* __restrict__ x_perm) {
+                                                      int max_rows, int row_bytes, int zero_padding,
+                                                      char* __restrict__ x_perm) {
   const int R = min(*offsets_end, max_rows);
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nwaves = gridDim.x * 4;
   for (int r = wave; r < R; r += nwaves) {
     const int t = perm_token[r];
-    if ((unsigned)t >= (unsigned)T) continue;
+    if ((unsigned)t >= (unsigned)T) {  // a padding slot
+      if (zero_padding) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        for (int off = lane * 16; off < row_bytes; off += 1024) st16(x_perm + (size_t)r * row_bytes + off, zero);
+      }
+      continue;
+    }
     const char* src = x + (size_t)t * row_bytes;
     char* dst = x_perm + (size_t)r * row_bytes;
     int off = lane * 16;
@@ -164,7 +184,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
 // All of histogram, scan and rank in one block, for T k <= 512 assignments (the
 // decode shapes): the same results as the three kernels above with one block.
 __global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __restrict__ idx, int64_t P, int k,
-                                                              int E, int64_t cap, int32_t* __restrict__ counts,
+                                                              int E, int64_t cap, int padded,
+                                                              int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_of,
                                                               int32_t* __restrict__ perm_token) {
@@ -198,8 +219,10 @@ __global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __re
     __syncthreads();
     src ^= 1;
   }
-  for (int i = tid; i < E; i += kBP) offsets[i + 1] = incl[src][i];
-  if (tid == 0) offsets[0] = 0;
+  if (!padded) {
+    for (int i = tid; i < E; i += kBP) offsets[i + 1] = incl[src][i];
+    if (tid == 0) offsets[0] = 0;
+  }
   if (tid >= P) return;
   int32_t row = -1;
   if (valid) {
@@ -207,7 +230,7 @@ __global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __re
     int rank = __popc(m[w] & (bit - 1u));
     for (int q = 0; q < w; ++q) rank += __popc(m[q]);
     if (cap < 0 || rank < cap) {
-      row = incl[src][e] - kept[e] + rank;
+      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept[e] + rank;
       perm_token[row] = tid / k;
     }
   }
@@ -224,19 +247,25 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int tpe = min(64, 1024 / ep);
   if (nblk == 1) {
     hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
-                       a.counts, a.offsets, a.row_of, a.perm_token);
+                       a.padded, a.counts, a.offsets, a.row_of, a.perm_token);
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, tpe,
-                       a.capacity, a.block_base, a.counts, a.offsets);
+                       a.capacity, a.padded, a.block_base, a.counts, a.offsets);
     hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
-                       a.block_base, a.offsets, a.row_of, a.perm_token);
+                       a.block_base, a.offsets, a.padded, a.row_of, a.perm_token);
+  }
+  if (a.padded) {
+    const int64_t slots = (int64_t)a.E * a.capacity;
+    const int64_t n = std::max<int64_t>(slots, a.E + 1);
+    hipLaunchKernelGGL(pad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a.counts, a.E,
+                       (int)a.capacity, a.offsets, a.perm_token);
   }
   if (a.x_perm == nullptr) return hipGetLastError();
-  const int max_rows = (int)P;
+  const int max_rows = a.padded ? (int)((int64_t)a.E * a.capacity) : (int)P;
   const int blocks = (int)std::min<int64_t>((max_rows + 3) / 4, 8192);
   hipLaunchKernelGGL(gather_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream,
-                     (const char*)a.x, a.perm_token, a.offsets + a.E, a.T, max_rows, a.row_bytes,
+                     (const char*)a.x, a.perm_token, a.offsets + a.E, a.T, max_rows, a.row_bytes, a.padded,
                      (char*)a.x_perm);
   return hipGetLastError();
 }

@@ -117,6 +117,25 @@ def test_permute_rejects_before_launch(kw, status):
     assert permute(**kw) == status
 
 
+def test_permute_padded_rejects_before_launch():
+    lib = _lib.load()
+
+    def call(**kw):
+        a = dict(idx=FAKE, T=4, k=2, E=8, cap=3, x=FAKE, dtype=1, d=128, counts=FAKE, offsets=FAKE, row_of=FAKE,
+                 slot=FAKE, xs=FAKE, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.moe_permute_padded(a["idx"], a["T"], a["k"], a["E"], a["cap"], a["x"], a["dtype"], a["d"],
+                                      a["counts"], a["offsets"], a["row_of"], a["slot"], a["xs"], a["ws"],
+                                      a["ws_bytes"], None)
+    assert call(cap=0) == -1
+    assert call(cap=-1) == -1
+    assert call(E=256, k=2, cap=2 ** 24) == -2
+    assert call(slot=None) == -1
+    assert call(x=None) == -1
+    assert call(ws=None) == -3
+    assert call(T=0, idx=None, slot=None, ws=None, ws_bytes=0) == 0
+
+
 def test_permute_zero_tokens_is_a_no_op():
     assert permute(T=0, idx=None, ws=None, ws_bytes=0) == 0
 
@@ -146,11 +165,12 @@ def test_grouped_zero_rows_is_a_no_op():
 
 def test_combine_and_stats_reject_before_launch():
     lib = _lib.load()
-    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, -1, 2, 128, FAKE, None) == -1
-    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, 4, 0, 128, FAKE, None) == -1
-    assert lib.moe_combine(FAKE, FAKE, FAKE, None, 1, 4, 2, 12, FAKE, None) == -2
-    assert lib.moe_combine(None, FAKE, FAKE, None, 1, 4, 2, 128, FAKE, None) == -1
-    assert lib.moe_combine(None, None, None, None, 1, 0, 2, 128, None, None) == 0
+    assert lib.moe_combine(FAKE, 8, FAKE, FAKE, None, 1, -1, 2, 128, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, 8, FAKE, FAKE, None, 1, 4, 0, 128, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, 8, FAKE, FAKE, None, 1, 4, 2, 12, FAKE, None) == -2
+    assert lib.moe_combine(None, 8, FAKE, FAKE, None, 1, 4, 2, 128, FAKE, None) == -1
+    assert lib.moe_combine(FAKE, -1, FAKE, FAKE, None, 1, 4, 2, 128, FAKE, None) == -1
+    assert lib.moe_combine(None, 0, None, None, None, 1, 0, 2, 128, None, None) == 0
     assert lib.moe_stats(FAKE, FAKE, 4, 2, 8, 0.01, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == -3
     assert lib.moe_stats(FAKE, FAKE, 4, 9, 8, 0.01, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert lib.moe_stats(FAKE, FAKE, 4, 2, 8, float("nan"), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1

@@ -206,6 +206,73 @@ def test_bias_balancing_loop_on_gpu():
     run.free()
 
 
+@pytest.mark.parametrize("T,E,k,phi", [(40, 8, 2, 1.0), (300, 16, 4, 0.8), (700, 8, 3, 1.25)])
+def test_padded_dispatch_matches_oracle(T, E, k, phi):
+    """Capacity-padded layout, bit-exact: counts, offsets e*C, slots (rank order,
+    -1 padding), row_of, and the gathered slot rows with zero padding."""
+    shape = S("padded", "bf16", T, 128, E, k, 128, 0, SM_TK, True, phi, False)
+    inp = minp.LayerInputs(shape, seed=2)
+    run = GpuRun(inp)
+    run.layer.route(run.x, run.bufs)
+    C = oracle.capacity(T, k, E, phi)
+    slot = torch.empty(E * C, dtype=torch.int32, device="cuda")
+    xs = torch.empty((E * C, shape.d), dtype=torch.bfloat16, device="cuda")
+    b = run.bufs
+    _lib.moe_permute_padded(b.topk_idx, T, k, E, C, run.x, shape.d, b.counts, b.offsets, b.row_of, slot, xs,
+                            b.ws_permute)
+    torch.cuda.synchronize()
+    idx = host(b.topk_idx)
+    counts, offsets, row_of, slot_token = oracle.dispatch_padded(idx, E, C)
+    assert np.array_equal(host(b.counts), counts)
+    assert np.array_equal(host(b.offsets), offsets)
+    assert np.array_equal(host(b.row_of), row_of)
+    assert np.array_equal(host(slot), slot_token)
+    x_ref = oracle.gather_slots(minp.as_f32(inp.x, "bf16"), slot_token)
+    assert np.array_equal(host(xs), x_ref)
+    run.free()
+
+
+@pytest.mark.parametrize("shape", [
+    S("padded_layer", "bf16", 600, 256, 8, 2, 256, 0, TK_SM, False, 1.0, False),
+    S("padded_layer_shared", "bf16", 500, 256, 16, 4, 384, 256, SM_TK, True, 1.25, False),
+], ids=lambda s: s.name)
+def test_padded_layout_layer_matches_compact(shape):
+    """The layer over the padded layout (grouped GEMMs over all E*C slots, offsets
+    e*C, rows gathered through slot_token) gives the same y as the compact layout,
+    bit for bit (every row is computed by the same kernel with the same K order),
+    and matches the oracle."""
+    inp = minp.LayerInputs(shape, seed=4)
+    run = GpuRun(inp)
+    out = run.run()                                     # the compact layout
+    y_compact = out["y"]
+    s, b, lay = shape, run.bufs, run.layer
+    C = oracle.capacity(s.T, s.k, s.E, s.phi)
+    slots = s.E * C
+    assert s.T * s.k > 32 * s.E and slots > 32 * s.E   # both layouts take the tile kernel
+    slot = torch.empty(slots, dtype=torch.int32, device="cuda")
+    a = torch.empty((slots, s.F), dtype=torch.bfloat16, device="cuda")
+    yp = torch.empty((slots, s.d), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((s.T, s.d), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_permute_padded(b.topk_idx, s.T, s.k, s.E, C, run.x, s.d, b.counts, b.offsets, b.row_of, slot, None,
+                            b.ws_permute)
+    w = run.weights
+    _lib.moe_grouped_gate_up(run.x, slot, s.T, b.offsets, s.E, slots, s.d, s.F, w.gate, w.up, a)
+    _lib.moe_grouped_down(a, b.offsets, s.E, slots, s.F, s.d, w.down, yp)
+    if s.F_shared:
+        lay.shared_expert(run.x, b)
+    _lib.moe_combine(yp, b.row_of, b.topk_w, b.shared_y if s.F_shared else None, s.T, s.k, s.d, y, y_rows=slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), y_compact)
+    ex = ExpertCache(inp)
+    full = oracle.layer_forward(minp.as_f32(inp.x, s.dtype), minp.as_f32(inp.w_router, s.dtype), inp.bias, ex,
+                                ex.shared(), k=s.k, mode=s.mode, renorm=s.renorm, phi=s.phi, alpha=s.alpha,
+                                dtype=s.dtype)
+    same = ~(out["idx"] != full["idx"]).any(1) & ~((out["near_tie"] == 1) | (full["near_tie"] == 1))
+    err = np.abs(host(y)[same] - full["y64"][same]).max()
+    assert err <= TOL[s.dtype] * np.abs(full["y64"]).max()
+    run.free()
+
+
 def test_zero_tokens_is_a_no_op():
     shape = SMALL[0].with_(T=0)
     inp = minp.LayerInputs(shape, seed=0)
