@@ -42,12 +42,12 @@ __global__ __launch_bounds__(kBP) void hist_kernel(const int32_t* __restrict__ i
   for (int e = tid; e < E; e += kBP) block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One block of 1024 threads.  tpe threads per expert split the block list into
-// contiguous chunks; chunk sums are scanned in LDS, then each thread writes the
+// One block of 1024 threads.  tpe threads per expert (thread c * ep + e) split the
+// block list into contiguous chunks; chunk sums are scanned in LDS, then each thread writes the
 // running base of its blocks; the kept counts are then scanned over experts in
 // LDS for the offsets.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
-                                                     int E, int tpe, int64_t cap, int padded,
+                                                     int E, int ep, int tpe, int64_t cap, int padded,
                                                      int32_t* __restrict__ block_base,
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets) {
@@ -55,8 +55,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   __shared__ int kept_s[2][MOE_MAX_EXPERTS];
   constexpr int kBatch = 16;  // loads in flight per thread
   const int tid = threadIdx.x;
-  const int e = tid / tpe, c = tid % tpe;
-  const bool active = e < E;
+  // expert fastest (ep >= E, a power of two): a wave reads 64 consecutive experts'
+  // counts of one block, one contiguous run, instead of 64 scattered words
+  const int e = tid % ep, c = tid / ep;
+  const bool active = e < E && c < tpe;
   const int chunk = (nblk + tpe - 1) / tpe;
   const int b0 = min(c * chunk, nblk), b1 = active ? min(b0 + chunk, nblk) : b0;
   const int ec = active ? e : 0;
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   __syncthreads();
   int base = 0;
   if (active)
-    for (int q = 0; q < c; ++q) base += part[e * tpe + q];
+    for (int q = 0; q < c; ++q) base += part[q * ep + e];
   for (int b = b0; b < b1; b += kBatch) {
     int v[kBatch];
 #pragma unroll
@@ -250,7 +252,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
                        a.padded, a.counts, a.offsets, a.row_of, a.perm_token);
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, tpe,
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, ep, tpe,
                        a.capacity, a.padded, a.block_base, a.counts, a.offsets);
     hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
                        a.block_base, a.offsets, a.padded, a.row_of, a.perm_token);

@@ -9,13 +9,16 @@
 // page, "Keeping the load even": a per-expert bias that only chooses.
 // Transformers & Math 17.2: the two softmax orders.
 //
-// Two launch shapes, chosen by T (bf16):
+// Launch shapes, chosen by T and E (bf16):
 //  * many tokens: one block of 4 waves takes 64 tokens and every expert (E <= 256,
 //    padded to EP = 16*NB); scores and selection in one kernel (below).
 //  * few tokens (T <= MOE_ROUTE_SPLIT_MAX_T): a grid over (16 tokens, 16 experts)
 //    tiles whose 8 waves each take every 8th 128-wide slice of d, summed in wave
 //    order through LDS, writes the scores; a second kernel selects from them.  At
 //    decode sizes this spreads the router matrix over many CUs instead of one.
+//  * many tokens and E > 64 (while T ceil(E / 64) <= 32768): the fused kernel's
+//    loop on 64-expert blocks (two fit on a CU) writes the scores, and the select
+//    kernel above selects.
 // The fused shape:
 //  * Scores (bf16): a 64 x EP MFMA GEMM (16x16x32 bf16, fp32 accumulate).  Each
 //    wave owns 16 tokens; router-weight chunks of 256 k-values (128 for E > 128)
@@ -40,6 +43,10 @@ constexpr int kTokens = 64;   // tokens per block of the fused kernel
 constexpr int kSplitWaves = 8;    // waves per block of the split score kernel
 constexpr int kSplitTile = 16;    // tokens and experts per block of the split score kernel
 constexpr int kSelectTokens = 16; // tokens per block of the select kernel
+constexpr int kScoreSplitExperts = 64;  // experts per score block when T is large and E > 64
+// Measured (router alone, MI355X): E = 128, T = 16384: 44 us split vs 50 fused; E = 256:
+// T = 2048 64 vs 166, T = 16384 212 vs 183 (x, d = 7168, read four times).
+constexpr int64_t kScoreSplitMaxRowReads = 32768;
 
 // K chunk per pipeline stage: large enough that each stage keeps many bytes in
 // flight (a stage round trip is latency-bound), small enough for two stages of
@@ -210,16 +217,23 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
   }
 }
 
-template <int NB, int SPL>
+// SELECT = false: block (i, j) scores tokens 64 i .. against experts EP j .. EP j +
+// EP - 1 and writes them; route_select_kernel selects afterwards (more, smaller
+// blocks: two fit on a CU).
+template <int NB, int SPL, bool SELECT>
 __global__ __launch_bounds__(256) void route_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm, float* __restrict__ logits,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ near_tie) {
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr_all, const float* __restrict__ bias,
+    const float* __restrict__ sel_bias, int T, int d, int E_all, int k, int mode, int renorm,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ near_tie) {
   using L = RouteLds<NB>;
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   uint16_t* ws = reinterpret_cast<uint16_t*>(smem);
   float* tile = reinterpret_cast<float*>(smem);
 
+  const int e0 = SELECT ? 0 : blockIdx.y * L::EP;  // first expert of the block
+  const int E = SELECT ? E_all : min(L::EP, E_all - e0);
+  const uint16_t* wr = wr_all + (size_t)e0 * d;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.x * kTokens;
   const int kg = lane >> 4;
@@ -285,6 +299,22 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     }
     __syncthreads();
     stage ^= 1;
+  }
+  if (!SELECT) {
+    // accumulator element i of lane l: token 16 wave + 4 (l / 16) + i, expert nb 16 + l % 16
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = nb * 16 + (lane & 15);
+      if (n < E) {
+        const float b = bias != nullptr ? bias[e0 + n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + wave * 16 + 4 * kg + i;
+          if (t < T) logits[(size_t)t * E_all + e0 + n] = acc[nb][i] + b;
+        }
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -404,8 +434,19 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((route_select_kernel<NB, SPL>), dim3((a.T + kSelectTokens - 1) / kSelectTokens), block, 0,
                        stream, a.T, a.E, a.k, a.mode, a.renorm, a.select_bias, a.logits, a.topk_idx, a.topk_w,
                        a.near_tie);
+  } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
+             (int64_t)a.T * ((a.E + kScoreSplitExperts - 1) / kScoreSplitExperts) <= kScoreSplitMaxRowReads) {
+    // many experts: 64-expert score blocks (two per CU), then selection; each block
+    // group re-reads x, so this stops paying once T x (E / 64) grows large
+    const dim3 sgrid((a.T + kTokens - 1) / kTokens, (a.E + kScoreSplitExperts - 1) / kScoreSplitExperts);
+    hipLaunchKernelGGL((route_bf16_kernel<kScoreSplitExperts / 16, 1, false>), sgrid, block, 0, stream,
+                       (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, nullptr, a.T, a.d, a.E, a.k,
+                       a.mode, a.renorm, a.logits, nullptr, nullptr, nullptr);
+    hipLaunchKernelGGL((route_select_kernel<NB, SPL>), dim3((a.T + kSelectTokens - 1) / kSelectTokens), block, 0,
+                       stream, a.T, a.E, a.k, a.mode, a.renorm, a.select_bias, a.logits, a.topk_idx, a.topk_w,
+                       a.near_tie);
   } else if (a.dtype == MOE_BF16)
-    hipLaunchKernelGGL((route_bf16_kernel<NB, SPL>), grid, block, 0, stream, (const uint16_t*)a.x,
+    hipLaunchKernelGGL((route_bf16_kernel<NB, SPL, true>), grid, block, 0, stream, (const uint16_t*)a.x,
                        (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
                        a.logits, a.topk_idx, a.topk_w, a.near_tie);
   else

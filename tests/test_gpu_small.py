@@ -44,6 +44,8 @@ SMALL = [
     S("many_tokens_softmax_biased", "bf16", 2100, 128, 64, 6, 128, 0, SM_TK, False, None, False,
       select_bias=0.01),
     S("f32_sigmoid_biased", "f32", 100, 72, 5, 2, 40, 0, SIG, False, None, False, select_bias=0.1),
+    # E = 256 with T (E / 64) past the split-score limit: the fused kernel with 256 experts
+    S("many_tokens_E256_fused", "bf16", 8300, 128, 256, 8, 128, 0, SM_TK, True, None, True, select_bias=0.002),
 ]
 
 
