@@ -389,8 +389,9 @@ constexpr int SK_ROWS = 16;   // B rows per MFMA tile
 // single, 4 waves x 32 rows (two 16-row sets).
 __host__ __device__ constexpr int sk_bn(bool dual) { return dual ? 64 : 128; }
 constexpr int SK_CHUNK = 128; // K per chunk
+constexpr int kSkinnyTwoTilesAbove = 10;  // rows per group (average) above which a pass takes two token tiles
 
-template <bool DUAL, bool GATHER>
+template <bool DUAL, bool GATHER, int TT>
 __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
@@ -414,8 +415,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
   // memory counter retires in order).  The loop prefetches the next pair while a
   // pair is multiplied; the last pair is peeled off, so no load sits under a branch
   // and none is wasted (an odd chunk count re-loads the last chunk once, as a
-  // second chunk multiplied with zeroed token values).
-  u32x4 wa[2][NB][4], ta[2][4];
+  // second chunk multiplied with zeroed token values).  Each weight chunk serves
+  // TT 16-row token tiles (rows past the group re-read its last row; their results
+  // are not stored).
+  u32x4 wa[2][NB][4], ta[2][TT][4];
+  const uint16_t* ap[TT];
   auto load_w = [&](int buf, int c) {
     const int k0 = min(c, nchunks - 1) * SK_CHUNK;
 #pragma unroll
@@ -424,74 +428,92 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
       wa[buf][1][u] = ld16(bu + k0 + 32 * u);
     }
   };
-  auto load_x = [&](int buf, int c, const uint16_t* ap) {
+  auto load_x = [&](int buf, int c) {
     const int k0 = min(c, nchunks - 1) * SK_CHUNK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ta[buf][u] = ld16(ap + k0 + 32 * u);
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ta[buf][tt][u] = ld16(ap[tt] + k0 + 32 * u);
   };
   const int npairs = (nchunks + 1) / 2;
-  for (int t0 = lo; t0 < hi; t0 += 16) {
+  for (int t0 = lo; t0 < hi; t0 += 16 * TT) {
     // an opaque zero keeps the first loads inside this loop (hoisted, they would be
     // drained by the first wait)
     int z;
     asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    int m = min(t0 + r16, hi - 1);
-    int mg = 0;
-    if (GATHER) mg = a_rows[m];
+    int m[TT], mg[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      m[tt] = min(t0 + 16 * tt + r16, hi - 1);
+      mg[tt] = 0;
+      if (GATHER) mg[tt] = a_rows[m[tt]];
+    }
     load_w(0, z);
-    if (GATHER) m = min(max(mg, 0), a_nrows - 1);
-    const uint16_t* ap = A + (size_t)m * K + 8 * q;
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      if (GATHER) m[tt] = min(max(mg[tt], 0), a_nrows - 1);
+      ap[tt] = A + (size_t)m[tt] * K + 8 * q;
+    }
     // issue order w0, x0, w1, x1 as in the loop (the scheduler would otherwise
     // reorder or sink the loads)
     __builtin_amdgcn_sched_barrier(0);
-    load_x(0, z, ap);
+    load_x(0, z);
     int z1 = z + 1;
-    asm volatile("" : "+s"(z1) : "v"(m));  // w1 after x0 (its index "depends" on the row)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) asm volatile("" : "+s"(z1) : "v"(m[tt]));  // w1 after x0
     __builtin_amdgcn_sched_barrier(0);
     load_w(1, z1);
-    load_x(1, z1, ap);
+    load_x(1, z1);
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[NB];
+    f32x4 acc[TT][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[tt][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto mma = [&](int buf, uint32_t keep) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          acc[b] = mfma16x16x32(as_bf16x8(wa[buf][b][u]), as_bf16x8(ta[buf][u] & keep), acc[b]);
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            acc[tt][b] = mfma16x16x32(as_bf16x8(wa[buf][b][u]), as_bf16x8(ta[buf][tt][u] & keep), acc[tt][b]);
     };
     for (int p = 0; p + 1 < npairs; ++p) {
       mma(0, ~0u);
       __builtin_amdgcn_sched_barrier(0);
       load_w(0, 2 * p + 2);
-      load_x(0, 2 * p + 2, ap);
+      load_x(0, 2 * p + 2);
       __builtin_amdgcn_sched_barrier(0);
       mma(1, ~0u);
       __builtin_amdgcn_sched_barrier(0);
       load_w(1, 2 * p + 3);
-      load_x(1, 2 * p + 3, ap);
+      load_x(1, 2 * p + 3);
       __builtin_amdgcn_sched_barrier(0);
     }
     mma(0, ~0u);
     mma(1, 2 * npairs <= nchunks ? ~0u : 0u);  // uniform
-    // acc[b] element i of lane l: B row 4 (l / 16) + i of set b, token row t0 + l % 16.
-    const int row = t0 + r16;
-    if (row < hi) {
-      uint16_t* crow = C + (size_t)row * N + n_base + 4 * q;
-      if (DUAL) {
-        float v[4];
+    // acc[tt][b] element i of lane l: B row 4 (l / 16) + i of set b, token row
+    // t0 + 16 tt + l % 16.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = acc[0][i];
-          v[i] = __fdividef(x, 1.f + __expf(-x)) * acc[1][i];
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = t0 + 16 * tt + r16;
+      if (row < hi) {
+        uint16_t* crow = C + (size_t)row * N + n_base + 4 * q;
+        if (DUAL) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = acc[tt][0][i];
+            v[i] = __fdividef(x, 1.f + __expf(-x)) * acc[tt][1][i];
+          }
+          *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            *reinterpret_cast<uint2*>(crow + b * SK_ROWS) =
+                make_uint2(pack_bf16x2(acc[tt][b][0], acc[tt][b][1]), pack_bf16x2(acc[tt][b][2], acc[tt][b][3]));
         }
-        *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-      } else {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-          *reinterpret_cast<uint2*>(crow + b * SK_ROWS) =
-              make_uint2(pack_bf16x2(acc[b][0], acc[b][1]), pack_bf16x2(acc[b][2], acc[b][3]));
       }
     }
   }
@@ -553,15 +575,24 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
     // few rows per group on average: stream the weights, skip the 256-row tiles
     const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
-#define MOE_SKINNY(D, GA)                                                                                    \
-  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA>), grid, block, 0, stream, (const uint16_t*)a.A,    \
+#define MOE_SKINNY(D, GA, TT)                                                                                \
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA, TT>), grid, block, 0, stream, (const uint16_t*)a.A, \
                      a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,     \
                      D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C)
     const bool gather = a.a_rows != nullptr;
-    if (dual && gather) MOE_SKINNY(true, true);
-    else if (dual) MOE_SKINNY(true, false);
-    else if (gather) MOE_SKINNY(false, true);
-    else MOE_SKINNY(false, false);
+    // two 16-row token tiles per weight pass once groups average over 10 rows (then
+    // many groups exceed 16 rows, and one tile per pass would stream their weights twice)
+    if ((int64_t)a.max_rows > (int64_t)kSkinnyTwoTilesAbove * a.G) {
+      if (dual && gather) MOE_SKINNY(true, true, 2);
+      else if (dual) MOE_SKINNY(true, false, 2);
+      else if (gather) MOE_SKINNY(false, true, 2);
+      else MOE_SKINNY(false, false, 2);
+    } else {
+      if (dual && gather) MOE_SKINNY(true, true, 1);
+      else if (dual) MOE_SKINNY(true, false, 1);
+      else if (gather) MOE_SKINNY(false, true, 1);
+      else MOE_SKINNY(false, false, 1);
+    }
 #undef MOE_SKINNY
     return hipGetLastError();
   }

@@ -287,7 +287,9 @@ def test_zero_tokens_is_a_no_op():
 @pytest.mark.parametrize("dtype,sizes", [
     ("bf16", [0, 1, 127, 128, 129, 300]),                      # 256-row tile kernel
     ("f32", [0, 1, 127, 128, 129, 300]),
-    ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7]),  # few rows per group: skinny kernel
+    ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7]),  # few rows per group: skinny kernel,
+                                                                # two token tiles per weight pass
+    ("bf16", [0, 1, 3, 16, 17, 2, 0, 5]),                      # skinny, one token tile per pass
 ])
 def test_grouped_gemm_hand_made_groups(dtype, sizes):
     """Ragged groups (empty, single row, tile edges), rows left outside every group,
