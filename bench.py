@@ -37,6 +37,9 @@ def parse():
     p.add_argument("--decode-workload", default="qwen3_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--configs", action="store_true",
+                   help="instead of the headline line, time the whole layer on every configured shape "
+                        "(one JSON line per shape; generating the largest weight set takes a while)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                    help="only copy BYTES bytes device to device three times (a plain copy kernel of known size "
                         "that scales the HBM byte counters) and exit")
@@ -163,10 +166,52 @@ def cpu_baseline(inp, target_s):
                       f"{elapsed:.1f} s"}
 
 
+def config_sweep(steps: int, warmup: int):
+    """Time the layer on every configured shape (synthetic inputs, seed 0): one
+    JSON line each with tokens/s, the routed and shared expert FLOPs against the
+    bf16 MFMA peak, and the algorithmic bytes against HBM."""
+    import torch
+
+    from mixture_experts_ffn_08_amd import inputs as minp
+    from mixture_experts_ffn_08_amd.layer import Buffers, DeviceWeights, MoeLayer, to_device
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    for name in ("mixtral", "mixtral_cap", "qwen2", "qwen3_prefill", "qwen3_decode", "dsv3_skew"):
+        shape = minp.SHAPES[name]
+        t0 = time.time()
+        inp = minp.LayerInputs(shape, seed=0)
+        weights = DeviceWeights(inp, "cuda:0")
+        layer = MoeLayer(weights)
+        x = to_device(inp.x, shape.dtype, "cuda:0")
+        bufs = Buffers(shape, shape.T, "cuda:0")
+        setup_s = time.time() - t0
+        with torch.cuda.stream(stream):
+            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch)
+        R = int(bufs.offsets[-1].item())
+        touched = int((bufs.counts > 0).sum().item())
+        s = shape
+        flops = 6.0 * R * s.d * s.F + 6.0 * s.T * s.d * s.F_shared + 2.0 * s.T * s.d * s.E
+        nbytes = (touched * 3 * s.d * s.F + 3 * s.d * s.F_shared + s.E * s.d + 2 * s.T * s.d) * s.elem_bytes
+        print(json.dumps({
+            "workload": name, "T": s.T, "d": s.d, "E": s.E, "k": s.k, "F": s.F, "F_shared": s.F_shared,
+            "capacity_factor": s.phi, "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3),
+            "gate_up_ms": gu_ms, "down_ms": dn_ms, "kept_assignments": R, "experts_touched": touched,
+            "max_over_mean": float(bufs.max_over_mean.item()),
+            "layer_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_mfma_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+            "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / PEAK_HBM_BYTES,
+            "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1)}), flush=True)
+        del weights, layer, x, bufs, inp
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.configs:
+        config_sweep(args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
