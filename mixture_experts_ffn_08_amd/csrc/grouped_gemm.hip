@@ -20,7 +20,9 @@
 //    register sets: the 16-byte loads of step kt+2 are issued while step kt is
 //    multiplied, because under full load a global round trip takes longer than one
 //    step of MFMA work.  One barrier per step, a plain s_barrier (a __syncthreads
-//    fence would also wait for the loads in flight).  LDS rows padded to 144 bytes:
+//    fence would also wait for the loads in flight), placed before the step's last
+//    16-wide k slice so that the next stage's first fragments are read while that
+//    slice is multiplied.  LDS rows padded to 144 bytes:
 //    conflict-free ds_read_b128.  Within a step, the fragments of the next 16-wide
 //    k slice are read while the current one is multiplied, and the step's global
 //    loads and LDS writes are spread between the MFMAs (one wave per SIMD: a wave
@@ -32,7 +34,9 @@
 //  * Persistent: one block per CU.  Tiles of all groups are enumerated on the
 //    device from offsets (no host round trip); each XCD (blocks are dealt
 //    round-robin to the 8 XCDs) owns a contiguous run of tiles that its blocks take
-//    in turn, so the same expert's weights and the same rows stay in that XCD's L2.
+//    in turn, and inside an expert the tiles run in bands of 4 m-tiles (down the
+//    band, then across n), so the tiles an XCD holds at once share their weight
+//    slices and their rows through that XCD's L2.
 //    The next tile's first two K steps are loaded while the current tile's output
 //    is stored.
 //  * Global loads are buffer loads (scalar resource, 32-bit lane offset, the K
@@ -87,9 +91,17 @@ __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_ro
   return s.incl[255];
 }
 
-// Group g holding m-tile mt (binary search on the inclusive prefix), its first row
-// and end row.
-__device__ void locate(int G, const TileScan& s, int mt, int& g, int& row0, int& row_end) {
+// Tile t -> group g, first row, end row and n-tile.  Group g owns the tiles
+// [excl n_tiles, incl n_tiles) (excl, incl: its m-tile prefix), so a binary search
+// for m-tile t / n_tiles on the inclusive prefix finds it.  Inside a group the
+// tiles run in bands of kBandRows m-tiles: down the band's m-tiles first, then
+// across the n-tiles, then the next band.  The tiles that the CUs of one XCD hold
+// at the same time then form a block of about 4 m-tiles x 8 n-tiles, whose A rows
+// and weight rows each sit once in that XCD's L2 and are read by several tiles
+// (m-tile-major order would stream a fresh weight slice for every tile).
+constexpr int kBandRows = 4;
+__device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int& row0, int& row_end, int& nt) {
+  const int mt = t / n_tiles;
   int lo = 0, hi = G - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
@@ -97,7 +109,11 @@ __device__ void locate(int G, const TileScan& s, int mt, int& g, int& row0, int&
   }
   g = lo;
   const int excl = g > 0 ? s.incl[g - 1] : 0;
-  row0 = s.start[g] + (mt - excl) * BM;
+  const int u = t - excl * n_tiles;                   // tile index inside the group
+  const int band = u / (kBandRows * n_tiles), v = u - band * (kBandRows * n_tiles);
+  const int h = min(kBandRows, s.incl[g] - excl - band * kBandRows);  // m-tiles in this band
+  nt = v / h;
+  row0 = s.start[g] + (band * kBandRows + v % h) * BM;
   row_end = s.start[g + 1];
 }
 
@@ -152,9 +168,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // single -> rows [n0, n0+256), or [n0, n0+128) twice for a last tile of 128
   // columns (the columns past N are not stored).
   auto setup = [&](int t) {
-    const int mt = t / n_tiles, nt = t % n_tiles;
-    int g;
-    locate(G, scan, mt, g, row0, row_end);
+    int g, nt;
+    locate(G, scan, n_tiles, t, g, row0, row_end, nt);
     g = __builtin_amdgcn_readfirstlane(g);  // block-uniform: keep the bases in scalar registers
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
@@ -255,8 +270,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // issued its 16 loads back to back would stall on the vector memory queue
     // with its MFMA unit idle.  Per k slice (fenced, so that fragment lifetimes
     // stay one slice long): 4 loads and the 8 fragment reads of the next slice
-    // (last slice: the 16 LDS writes of the next stage), each load or pair of
-    // LDS operations followed by MFMAs.
+    // (third slice: also the 16 LDS writes of the next stage), each load or group
+    // of LDS operations followed by MFMAs.  The step's barrier sits before the
+    // last slice.
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -268,10 +284,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       }
     };
     using DsRead = std::integral_constant<int, 0x100>;
-    using DsWrite = std::integral_constant<int, 0x200>;
-    using Zero = std::integral_constant<int, 0>;
+    using AnyDs = std::integral_constant<int, 0x080>;
     using Two = std::integral_constant<int, 2>;
-    using Four = std::integral_constant<int, 4>;
+    using Six = std::integral_constant<int, 6>;
     read_frags(st, 16, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 0);
     mma(0);
@@ -284,19 +299,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 2);
-    mma(0);
-    slice_pattern(DsRead{}, Two{});
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE == kFull) load_part(set, kn, 3);
     if constexpr (MODE != kLast) store(Other{}, S ^ 1);
-    mma(1);
+    mma(0);
+    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Six{}); else slice_pattern(DsRead{}, Two{});
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (MODE != kLast) {
-      slice_pattern(DsWrite{}, Four{});
+      // Every wave has read its last fragments of this stage and written the next
+      // one: after the barrier the next stage's first fragments are read while the
+      // last slice is multiplied, so no wave waits on LDS at the step boundary.
       lds_barrier();
       read_frags(lds + (S ^ 1) * STAGE, 0, 0);
-    } else {
-      slice_pattern(DsWrite{}, Zero{});
     }
+    if constexpr (MODE == kFull) load_part(set, kn, 3);
+    mma(1);
+    slice_pattern(DsRead{}, std::integral_constant<int, MODE != kLast ? 2 : 0>{});
   };
 
   using Full = std::integral_constant<int, kFull>;
