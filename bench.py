@@ -32,7 +32,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="qwen3_prefill")
     p.add_argument("--decode-workload", default="qwen3_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")

@@ -27,6 +27,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Fourth word of a gfx9-family buffer resource: raw (untyped) 32-bit access.
+constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // 32x32 output, K = 16 per instruction.  Lane l supplies A row (l % 32) and B

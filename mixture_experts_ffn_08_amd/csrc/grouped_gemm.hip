@@ -55,8 +55,6 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;             // bf16 elements per LDS row (16-byte pad)
 constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
 constexpr int kXcds = 8;
-// Fourth word of a gfx9-family buffer resource: raw (untyped) 32-bit access.
-constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
 

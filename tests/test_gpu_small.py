@@ -32,8 +32,13 @@ SMALL = [
     S("E256", "bf16", 130, 128, 256, 8, 128, 0, SM_TK, True, None, True),
     S("k_over_64", "bf16", 40, 128, 200, 70, 128, 0, TK_SM, False, None, False),
     S("tiny_capacity_f32", "f32", 64, 64, 8, 2, 128, 0, TK_SM, False, 1.25, False),
-    # above the router's few-token threshold: scores and selection in one kernel
+    # above the router's few-token threshold (E > 64: score blocks of 64 experts, then selection;
+    # else scores and selection in one kernel), with d / 128 odd and even
     S("many_tokens", "bf16", 2100, 128, 16, 4, 128, 0, SM_TK, True, None, False),
+    S("many_tokens_E128_d640", "bf16", 2200, 640, 128, 8, 128, 0, SM_TK, True, None, False),
+    S("many_tokens_E32_d896_topk_first", "bf16", 2111, 896, 32, 4, 128, 0, TK_SM, False, None, False,
+      select_bias=0.02),
+    S("many_tokens_E256_d384_sigmoid", "bf16", 2500, 384, 256, 8, 128, 0, SIG, False, None, False),
     S("many_tokens_E200_k70", "bf16", 2070, 128, 200, 70, 128, 0, TK_SM, False, None, False),
     # sigmoid scoring and the selection-only bias, in each mode and both router shapes
     S("sigmoid", "bf16", 300, 256, 16, 4, 256, 0, SIG, False, None, False),
