@@ -93,34 +93,30 @@ def copy_probe(nbytes: int):
 
 
 def timed_steps(layer, x, bufs, steps, warmup, stream, torch):
-    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down)."""
+    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down).
+    With large groups the balance statistics run on a second stream beside the
+    combine (MoeLayer.forward); a step ends when both streams are done.  The timed
+    steps record no events inside; the per-launch GEMM times come from as many
+    further steps with events around the two launches."""
+    side = torch.cuda.Stream()
+
     def step(ev=None):
-        layer.route(x, bufs, stream)
-        layer.permute(x, bufs, stream)
-        if ev is not None:
-            ev[0].record(stream)
-        layer.gate_up(x, bufs, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        layer.down(bufs, stream)
-        if ev is not None:
-            ev[2].record(stream)
-        layer.shared_expert(x, bufs, stream)
-        layer.combine(bufs, stream)
-        layer.stats(bufs, stream)
+        layer.forward(x, bufs, stream, side_stream=side, marks=ev)
 
     for _ in range(warmup):
         step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     gu = [e[0].elapsed_time(e[1]) for e in evs]
     dn = [e[1].elapsed_time(e[2]) for e in evs]
     return total / steps, float(np.mean(gu)), float(np.mean(dn))

@@ -280,6 +280,27 @@ def test_padded_layout_layer_matches_compact(shape):
     run.free()
 
 
+@pytest.mark.parametrize("name", ["small_zipf", "small_renorm", "small_shared"])
+def test_statistics_on_a_side_stream_match_serial(name):
+    """forward() given a second stream (the statistics fork before the combine when
+    groups are large, stay serial when small) gives bit-identical outputs to the
+    serial chain, over repeated steps on the same buffers."""
+    shape = next(s for s in SMALL if s.name == name)
+    inp = minp.LayerInputs(shape, seed=5)
+    run = GpuRun(inp)
+    ref = run.run()
+    main, side = torch.cuda.Stream(), torch.cuda.Stream()
+    for step in range(3):
+        run.layer.forward(run.x, run.bufs, main, side_stream=side)
+        main.synchronize()
+        b = run.bufs
+        for key, t in [("y", b.y), ("f", b.f), ("P", b.P), ("counts", b.counts), ("scores", b.logits)]:
+            assert np.array_equal(host(t), ref[key]), f"{key} differs at step {step}"
+        assert host(b.l_aux)[0] == ref["l_aux"] and host(b.max_over_mean)[0] == ref["max_over_mean"]
+    log(f"[{name}] side-stream statistics bit-identical over 3 steps")
+    run.free()
+
+
 def test_zero_tokens_is_a_no_op():
     shape = SMALL[0].with_(T=0)
     inp = minp.LayerInputs(shape, seed=0)
