@@ -30,6 +30,11 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 
 // Fourth word of a gfx9-family buffer resource: raw (untyped) 32-bit access.
 constexpr int kBufferFlags = 0x00020000;
+
+// Block barrier without the memory fence of __syncthreads (which would also wait
+// for the global loads still in flight): LDS writes are drained first, and the
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // 32x32 output, K = 16 per instruction.  Lane l supplies A row (l % 32) and B

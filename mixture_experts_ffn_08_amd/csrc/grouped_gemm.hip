@@ -115,10 +115,6 @@ __device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int
   row_end = s.start[g + 1];
 }
 
-// Block barrier without the memory fence of __syncthreads (which would also wait
-// for the global loads still in flight): LDS writes are drained first, and the
-// memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <bool DUAL>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(

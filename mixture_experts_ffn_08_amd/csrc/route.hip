@@ -21,14 +21,18 @@
 //    kernel above selects.
 // The fused shape:
 //  * Scores (bf16): a 64 x EP MFMA GEMM (16x16x32 bf16, fp32 accumulate).  Each
-//    wave owns 16 tokens; router-weight chunks of 256 k-values (128 for E > 128)
-//    are staged in a double-buffered LDS ring shared by the 4 waves, and the next
-//    chunk (and the next x operands) are fetched into registers while the current
-//    one is multiplied.  fp32 inputs take a plain FMA loop.
+//    wave owns 16 tokens, whose x operands it loads straight into registers; the
+//    router rows of each 64-wide k stage go through LDS (two stages), shared by
+//    the 4 waves.  Loads run in a register ring 4 or 6 stages deep with no
+//    branch and no drain in the loop: the kernel does little arithmetic per byte,
+//    so it needs many bytes in flight (one round trip per stage cost 40% more).
+//    fp32 inputs take a plain FMA loop.
 //  * Selection: the fp32 score tile goes to LDS; each 16-lane row of a wave takes
 //    one token (4 tokens per wave at once), lane r holding experts r + 16 i.
 //    k+1 rounds of arg-max over (score, -index) with DPP butterflies inside the
 //    row; the owner lane retires each winner.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -44,26 +48,28 @@ constexpr int kSplitWaves = 8;    // waves per block of the split score kernel
 constexpr int kSplitTile = 16;    // tokens and experts per block of the split score kernel
 constexpr int kSelectTokens = 16; // tokens per block of the select kernel
 constexpr int kScoreSplitExperts = 64;  // experts per score block when T is large and E > 64
-// Measured (router alone, MI355X): E = 128, T = 16384: 44 us split vs 50 fused; E = 256:
-// T = 2048 64 vs 166, T = 16384 212 vs 183 (x, d = 7168, read four times).
+// Measured (router with selection, MI355X, split vs fused): E = 128, d = 2048: T = 4096 21.5
+// vs 37.6 us, T = 16384 39.5 vs 41.3; E = 256, d = 7168: T = 4096 48 vs 134, T = 16384 180
+// vs 146 (x read four times).
 constexpr int64_t kScoreSplitMaxRowReads = 32768;
 
-// K chunk per pipeline stage: large enough that each stage keeps many bytes in
-// flight (a stage round trip is latency-bound), small enough for two stages of
-// router weights in LDS.
+// Router-weight staging: 64 k per stage, rows padded to 72 bf16 (conflict-free
+// 16-byte fragment reads); at least 32 rows so that every thread stores one
+// 16-byte chunk per stage (rows past E hold zeros).  The score kernel keeps kRing
+// stages of loads in flight in registers: its arithmetic per byte is low, so
+// only many bytes in flight per CU hide the memory latency.
 template <int NB>
 struct RouteLds {
   static constexpr int EP = NB * 16;
-  static constexpr int BK = EP <= 128 ? 256 : 128;
-  static constexpr int kWsStride = BK + 8;               // bf16 per staged router row (16-byte pad)
+  static constexpr int BK = 64;
+  static constexpr int kRows = EP > 32 ? EP : 32;
+  static constexpr int kWsStride = BK + 8;
+  static constexpr int kChunksPerThread = kRows * (BK / 8) / 256;
+  static constexpr int kRing = NB <= 8 ? 6 : 4;
   static constexpr int kTileStride = EP + 4;             // floats; breaks 4-row bank aliasing
   static constexpr int kTileBytes = kTokens * kTileStride * 4;
-  static constexpr int kWsBytes = 2 * EP * kWsStride * 2;  // two stages
+  static constexpr int kWsBytes = 2 * kRows * kWsStride * 2;  // two stages
   static constexpr int kBytes = kTileBytes > kWsBytes ? kTileBytes : kWsBytes;
-  static constexpr int kRowChunks = BK / 8;              // 16-byte chunks per router row per stage
-  static constexpr int kChunks = EP * kRowChunks;
-  static constexpr int kChunksPerThread = (kChunks + 255) / 256;
-  static constexpr int kSteps = BK / 32;                 // MFMA k-steps per stage
 };
 
 // a beats b: larger key, or equal key and lower expert index.
@@ -227,79 +233,123 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ near_tie) {
   using L = RouteLds<NB>;
+  constexpr int R = L::kRing, CPT = L::kChunksPerThread;
   __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   uint16_t* ws = reinterpret_cast<uint16_t*>(smem);
   float* tile = reinterpret_cast<float*>(smem);
 
   const int e0 = SELECT ? 0 : blockIdx.y * L::EP;  // first expert of the block
   const int E = SELECT ? E_all : min(L::EP, E_all - e0);
-  const uint16_t* wr = wr_all + (size_t)e0 * d;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kTokens;
   const int kg = lane >> 4;
-  const int arow = min(t0 + wave * 16 + (lane & 15), T - 1);
-  const uint16_t* xrow = x + (size_t)arow * d;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int t0 = blockIdx.x * kTokens;
+  const int rows = min(kTokens, T - t0);
+  const int nst = d / L::BK;  // d % 128 == 0
+  // Buffer resources over the block's token rows and its experts' router rows;
+  // 32-bit lane offsets, the stage's k offset as the uniform offset.
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (size_t)t0 * d), (short)0, (int)((uint32_t)rows * (uint32_t)d * 2u), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wr_all + (size_t)e0 * d), (short)0, (int)((uint32_t)E * (uint32_t)d * 2u), kBufferFlags);
+  constexpr uint32_t kOut = 0x80000000u;  // an offset past every resource: reads zeros
+  // x operand (16x16x32 MFMA "A"): token row wave 16 + lane % 16, k = 8 (lane / 16) + 32 q.
+  const uint32_t xoff = ((uint32_t)min(wave * 16 + (lane & 15), rows - 1) * (uint32_t)d + 8u * kg) * 2u;
+  // Router chunk i of this thread: c = tid + 256 i, row c / 8, k 8 (c % 8).
+  uint32_t woff[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = tid + 256 * i, n = c >> 3;
+    woff[i] = n < E ? ((uint32_t)n * (uint32_t)d + 8u * (c & 7)) * 2u : kOut;
+  }
 
-  // Router-weight chunk c of a stage: row n = c / kRowChunks, k offset 8 * (c % kRowChunks).
-  u32x4 wreg[L::kChunksPerThread];
-  auto load_w = [&](int k0) {
+  // Stage s into register set P.  Stages past the end (the loop runs in whole
+  // rings) read x as zeros and keep the last stage's k offset (inside both buffers).
+  u32x4 xr[R][2], wreg[R][CPT];
+  auto load = [&](auto set, int s) {
+    constexpr int P = decltype(set)::value;
+    const int kb = 2 * L::BK * min(s, nst - 1);
+    const uint32_t pad = s < nst ? 0u : kOut;
 #pragma unroll
-    for (int i = 0; i < L::kChunksPerThread; ++i) {
+    for (int q = 0; q < 2; ++q)
+      xr[P][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)((xoff + 64u * q) | pad),
+                                                                                  kb, 0));
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      wreg[P][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)woff[i], kb, 0));
+  };
+  auto store_w = [&](auto set, int stage) {
+    constexpr int P = decltype(set)::value;
+    uint16_t* dst = ws + stage * (L::kRows * L::kWsStride);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
       const int c = tid + 256 * i;
-      const int n = c / L::kRowChunks, kc = k0 + 8 * (c % L::kRowChunks);
-      wreg[i] = (c < L::kChunks && n < E && kc < d) ? ld16(wr + (size_t)n * d + kc) : zero;
+      st16(dst + (c >> 3) * L::kWsStride + 8 * (c & 7), wreg[P][i]);
     }
   };
-  auto store_w = [&](int stage) {
-    uint16_t* dst = ws + stage * (L::EP * L::kWsStride);
-#pragma unroll
-    for (int i = 0; i < L::kChunksPerThread; ++i) {
-      const int c = tid + 256 * i;
-      if (c < L::kChunks) st16(dst + (c / L::kRowChunks) * L::kWsStride + 8 * (c % L::kRowChunks), wreg[i]);
-    }
-  };
-  // x operand of k-step s of the stage: 8 values at k0 + 32 s + 8 kg of this lane's token.
-  u32x4 areg[L::kSteps], anext[L::kSteps];
-  auto load_a = [&](int k0, u32x4* dst) {
-#pragma unroll
-    for (int s = 0; s < L::kSteps; ++s) {
-      const int ka = k0 + 32 * s + 8 * kg;
-      dst[s] = ka < d ? ld16(xrow + ka) : zero;
-    }
-  };
-
   f32x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  load_a(0, areg);
-  load_w(0);
-  store_w(0);
-  __syncthreads();
-  int stage = 0;
-  for (int k0 = 0; k0 < d; k0 += L::BK) {
-    const bool more = k0 + L::BK < d;
-    if (more) {
-      load_a(k0 + L::BK, anext);
-      load_w(k0 + L::BK);
-    }
-    const uint16_t* cur = ws + stage * (L::EP * L::kWsStride);
+  auto mma = [&](auto set, int stage) {
+    constexpr int P = decltype(set)::value;
+    const uint16_t* cur = ws + stage * (L::kRows * L::kWsStride);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const uint16_t* brow = cur + (nb * 16 + (lane & 15)) * L::kWsStride + 8 * kg;
 #pragma unroll
-      for (int s = 0; s < L::kSteps; ++s)
-        acc[nb] = mfma16x16x32(as_bf16x8(areg[s]), as_bf16x8(ld16(brow + 32 * s)), acc[nb]);
+      for (int q = 0; q < 2; ++q) acc[nb] = mfma16x16x32(as_bf16x8(xr[P][q]), as_bf16x8(ld16(brow + 32 * q)), acc[nb]);
     }
-    if (more) {
-      store_w(stage ^ 1);
-#pragma unroll
-      for (int s = 0; s < L::kSteps; ++s) areg[s] = anext[s];
-    }
-    __syncthreads();
-    stage ^= 1;
+  };
+  // Step s (register set J, LDS stage s & 1): multiply; refill set J with stage
+  // s + R; store the router rows of stage s + 1 (set J + 1, loaded R - 1 steps
+  // ago) to the other LDS stage; one fence-free barrier.  No branch anywhere in
+  // the loop: the compiler's wait counts then leave R - 1 stages in flight.
+  auto step = [&](auto set, int s) {
+    constexpr int J = decltype(set)::value;
+    using Next = std::integral_constant<int, (J + 1) % R>;
+    mma(set, s & 1);
+    load(set, s + R);
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(Next{}, (s + 1) & 1);
+    lds_barrier();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  using C4 = std::integral_constant<int, 4 % R>;
+  using C5 = std::integral_constant<int, 5 % R>;
+  // Prologue in ring order (the loop head's wait counts merge with it).
+  load(C0{}, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(C1{}, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load(C2{}, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  load(C3{}, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (R > 4) {
+    load(C4{}, 4);
+    __builtin_amdgcn_sched_barrier(0);
+    load(C5{}, 5);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  store_w(C0{}, 0);
+  lds_barrier();
+  // nst >= 2: a do-while leaves no guard branch for the compiler to sink the
+  // prologue's loads behind (which would break their ring order).
+  int s0 = 0;
+  do {
+    step(C0{}, s0);
+    step(C1{}, s0 + 1);
+    step(C2{}, s0 + 2);
+    step(C3{}, s0 + 3);
+    if constexpr (R > 4) {
+      step(C4{}, s0 + 4);
+      step(C5{}, s0 + 5);
+    }
+    s0 += R;
+  } while (s0 < nst);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last ring's loads (past the end) land before exit
   if (!SELECT) {
     // accumulator element i of lane l: token 16 wave + 4 (l / 16) + i, expert nb 16 + l % 16
 #pragma unroll
