@@ -92,6 +92,26 @@ def copy_probe(nbytes: int):
     print(json.dumps({"copy_probe_bytes": nbytes}), flush=True)
 
 
+def measured_copy_rate(torch, nbytes: int = 1 << 30) -> float:
+    """Bytes moved per second (read + write) by a plain device-to-device copy of
+    nbytes: what streaming through HBM reaches on this part, beside the spec."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    rate = 2.0 * nbytes / (e0.elapsed_time(e1) / 10 * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
 def timed_steps(layer, x, bufs, steps, warmup, stream, torch):
     """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down).
     With large groups the balance statistics run on a second stream beside the
@@ -268,9 +288,12 @@ def main():
             dms, _, _ = timed_steps(dlayer, dx, dbufs, max(args.steps, 50), args.warmup, stream, torch)
         touched = int((dbufs.counts > 0).sum().item())
         dbytes = (touched * 3 * dshape.d * dshape.F + dshape.E * dshape.d + 2 * dshape.T * dshape.d) * 2
+        copy_rate = measured_copy_rate(torch)
         result["decode"] = {"workload": f"{dshape.name}: T={dshape.T}", "tokens_per_s": dshape.T / (dms * 1e-3),
                             "ms_per_step": dms, "experts_touched": touched, "algorithmic_bytes": dbytes,
-                            "hbm_frac": dbytes / (dms * 1e-3) / PEAK_HBM_BYTES}
+                            "hbm_frac": dbytes / (dms * 1e-3) / PEAK_HBM_BYTES,
+                            "measured_copy_TBps": copy_rate / 1e12,
+                            "frac_of_measured_copy": dbytes / (dms * 1e-3) / copy_rate}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
