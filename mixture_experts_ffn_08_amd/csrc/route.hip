@@ -17,7 +17,7 @@
 //    order through LDS, writes the scores; a second kernel selects from them.  At
 //    decode sizes this spreads the router matrix over many CUs instead of one.
 //  * many tokens and E > 64 (while T ceil(E / 64) <= 32768): the fused kernel's
-//    loop on 64-expert blocks (two fit on a CU) writes the scores, and the select
+//    loop on 64-expert blocks (three fit on a CU) writes the scores, and the select
 //    kernel above selects.
 // The fused shape:
 //  * Scores (bf16): a 64 x EP MFMA GEMM (16x16x32 bf16, fp32 accumulate).  Each
