@@ -30,6 +30,7 @@ SMALL = [
     S("k_equals_E", "bf16", 70, 128, 4, 4, 128, 0, SM_TK, True, None, False),
     S("one_token", "bf16", 1, 256, 16, 4, 256, 256, SM_TK, True, None, False),
     S("E256", "bf16", 130, 128, 256, 8, 128, 0, SM_TK, True, None, True),
+    S("E256_few_tokens", "bf16", 50, 256, 256, 8, 128, 0, SIG, False, None, False, select_bias=0.01),
     S("k_over_64", "bf16", 40, 128, 200, 70, 128, 0, TK_SM, False, None, False),
     S("tiny_capacity_f32", "f32", 64, 64, 8, 2, 128, 0, TK_SM, False, 1.25, False),
     # above the router's few-token threshold (E > 64: score blocks of 64 experts, then selection;
