@@ -62,7 +62,7 @@ struct GroupedGemmArgs {
 };
 // dual = true: C = SiLU(A B0^T) * (A B1^T); dual = false: C = A B0^T.
 // bf16 launches with max_rows <= kSkinnyRowsPerGroup * G use the skinny kernel.
-constexpr int kSkinnyRowsPerGroup = 32;
+constexpr int kSkinnyRowsPerGroup = 16;
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream);
 
 struct CombineArgs {

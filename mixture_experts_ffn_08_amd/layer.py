@@ -103,7 +103,7 @@ class Buffers:
 
 # Groups averaging at most this many rows (the weight-streaming GEMM regime) keep
 # the statistics on the main stream.
-SMALL_GROUP_ROWS = 32
+SMALL_GROUP_ROWS = 16
 
 
 class MoeLayer:
