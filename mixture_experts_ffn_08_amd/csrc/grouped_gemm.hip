@@ -51,9 +51,12 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int LDS_STRIDE = BK + 8;             // bf16 elements per LDS row (16-byte pad)
-constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
+constexpr int BN = 256, BK = 64;
+constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
+// Block tile rows: 256, or 128 when groups are small (at most kSmallTileRowsPerGroup
+// rows per group on average): a 256-row tile then holds mostly padding rows, and
+// a tile's time follows the bytes it streams (A rows + weight rows), not its MFMAs.
+constexpr int kSmallTileRowsPerGroup = 80;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
@@ -66,6 +69,7 @@ struct TileScan {
 
 // Block-wide: per-group m-tile counts, their inclusive prefix and the clamped group
 // bounds; returns the total.
+template <int BM>
 __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, TileScan& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = 0;
@@ -98,6 +102,7 @@ __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_ro
 // and weight rows each sit once in that XCD's L2 and are read by several tiles
 // (m-tile-major order would stream a fresh weight slice for every tile).
 constexpr int kBandRows = 4;
+template <int BM>
 __device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int& row0, int& row_end, int& nt) {
   const int mt = t / n_tiles;
   int lo = 0, hi = G - 1;
@@ -116,15 +121,22 @@ __device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int
 }
 
 
-template <bool DUAL>
+template <bool DUAL, int BM>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int n_tiles) {
+  constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
+  constexpr int NAC = BM / 32;                   // A chunks per thread per K step
+  // Wave layout.  BM = 256: the 4 waves as 2 x 2, each 128 rows x 128 B rows (dual:
+  // 64 gate rows and the same 64 up rows), 4 x 4 fragments of 32.  BM = 128: the 4
+  // waves split the B rows four ways, each 128 rows x 64 B rows (dual: 32 gate and
+  // the same 32 up rows), 4 x 2 fragments.
+  constexpr int NBF = BM == 256 ? 4 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
   __shared__ TileScan scan;
 
-  const int total = scan_tiles(offsets, G, max_rows, scan) * n_tiles;
+  const int total = scan_tiles<BM>(offsets, G, max_rows, scan) * n_tiles;
   // Persistent schedule.  Hardware block b runs on XCD b % 8 (blocks are dealt
   // round-robin); XCD x owns the contiguous tile run [x per, (x + 1) per) and its
   // blocks take the run's tiles in turn, so the CUs of an XCD work on neighbouring
@@ -140,8 +152,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int nk = K / BK;  // even: K % 128 == 0
 
-  // Copy mapping: each operand tile is 256 rows x 8 chunks of 16 bytes; thread tid
-  // moves chunks tid + 256 i: row (tid >> 3) + 32 i, k offset 8 (tid & 7).
+  // Copy mapping: an operand tile is BM (A) or 256 (B) rows x 8 chunks of 16 bytes;
+  // thread tid moves chunks tid + 256 i: row (tid >> 3) + 32 i, k offset 8 (tid & 7).
   // Addresses: block-uniform bases (scalar registers) plus 32-bit byte offsets per
   // thread (the host checks that every operand fits in 4 GiB).
   const int crow = tid >> 3, ccol = 8 * (tid & 7);
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const __amdgpu_buffer_rsrc_t rsrc_a =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, (int)((uint32_t)a_nrows * (uint32_t)K * 2u), kBufferFlags);
   __amdgpu_buffer_rsrc_t rsrc_b0, rsrc_b1;
-  uint32_t a_off8[8];
+  uint32_t a_off8[NAC];
   // B chunk i of this thread: row (first row of the tile) + crow + 32 (i & b_mask),
   // i.e. the lane offset b_lane plus the block-uniform step (i & b_mask) * b_step.
   const uint32_t b_lane = ((uint32_t)crow * (uint32_t)K + ccol) * 2u;
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // columns (the columns past N are not stored).
   auto setup = [&](int t) {
     int g, nt;
-    locate(G, scan, n_tiles, t, g, row0, row_end, nt);
+    locate<BM>(G, scan, n_tiles, t, g, row0, row_end, nt);
     g = __builtin_amdgcn_readfirstlane(g);  // block-uniform: keep the bases in scalar registers
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
@@ -175,30 +187,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
                                                        kBufferFlags)
                    : rsrc_b0;
     b_mask = (DUAL || n0 + BN > N) ? 3 : 7;
-    int arow[8];
+    int arow[NAC];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
-    if (a_rows != nullptr) {  // gather through the row index: 8 loads in flight, one wait
-      int v[8];
+    for (int i = 0; i < NAC; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
+    if (a_rows != nullptr) {  // gather through the row index: all loads in flight, one wait
+      int v[NAC];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = a_rows[arow[i]];
+      for (int i = 0; i < NAC; ++i) v[i] = a_rows[arow[i]];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
+      for (int i = 0; i < NAC; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
+    for (int i = 0; i < NAC; ++i) a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
   };
 
   // Two register sets: the loads of K step kt+2 are issued while step kt is
   // multiplied and step kt+1 is still in flight.
-  u32x4 ra[2][8], rb[2][8];
+  u32x4 ra[2][NAC], rb[2][8];
   // Quarter q of a K step's loads: A and B chunks 2q and 2q + 1.
   auto load_part = [&](auto set, int k0, int q) {
     constexpr int S = decltype(set)::value;
     const int kb = k0 * 2;
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      ra[S][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (int)a_off8[i], kb, 0));
+      if (i < NAC)
+        ra[S][i % NAC] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, (int)a_off8[i % NAC], kb, 0));
       rb[S][i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(DUAL && i >= 4 ? rsrc_b1 : rsrc_b0, (int)b_lane,
                                                        kb + (int)((i & b_mask) * b_step), 0));
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     uint16_t* sb = sa + BM * LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      st16(sa + (crow + 32 * i) * LDS_STRIDE + ccol, ra[S][i]);
+      if (i < NAC) st16(sa + (crow + 32 * i) * LDS_STRIDE + ccol, ra[S][i % NAC]);
       st16(sb + (crow + 32 * i) * LDS_STRIDE + ccol, rb[S][i]);
     }
   };
@@ -224,11 +238,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int frow = lane & 31, half = lane >> 5, fk = 8 * half;
   int a_off[4], b_off[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = (wm * 128 + i * 32 + frow) * LDS_STRIDE + fk;
+  for (int i = 0; i < 4; ++i) a_off[i] = ((BM == 256 ? wm * 128 : 0) + i * 32 + frow) * LDS_STRIDE + fk;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // dual: fragments 0,1 = gate rows wn*64 + {0,32}; 2,3 = the same rows of up
-    const int brow = DUAL ? (j >> 1) * (BN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32;
+  for (int j = 0; j < NBF; ++j) {
+    // BM = 256, dual: fragments 0,1 = gate rows wn*64 + {0,32}; 2,3 = the same rows of up.
+    // BM = 128, dual: fragment 0 = gate rows 32 wave .., 1 = the same rows of up.
+    const int brow = BM == 256 ? (DUAL ? (j >> 1) * (BN / 2) + wn * 64 + (j & 1) * 32 : wn * 128 + j * 32)
+                               : (DUAL ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32);
     b_off[j] = (BM + brow + frow) * LDS_STRIDE + fk;
   }
   bf16x8 fa[2][4], fb[2][4];
@@ -236,13 +252,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[buf][i] = as_bf16x8(ld16(st + a_off[i] + ks));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) fb[buf][j] = as_bf16x8(ld16(st + b_off[j] + ks));
+    for (int j = 0; j < NBF; ++j) fb[buf][j] = as_bf16x8(ld16(st + b_off[j] + ks));
   };
   auto mma = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(fb[buf][j], fa[buf][i], acc[i][j]);
+      for (int j = 0; j < NBF; ++j) acc[i][j] = mfma32x32x16(fb[buf][j], fa[buf][i], acc[i][j]);
   };
 
   using R0 = std::integral_constant<int, 0>;
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     using Other = std::integral_constant<int, S ^ 1>;
     const int kn = (kt + 2) * BK;
     const uint16_t* st = lds + S * STAGE;
-    // The global loads and LDS traffic are spread over the 64 MFMAs: a wave that
+    // The global loads and LDS traffic are spread over the MFMAs: a wave that
     // issued its 16 loads back to back would stall on the vector memory queue
     // with its MFMA unit idle.  Per k slice (fenced, so that fragment lifetimes
     // stay one slice long): 4 loads and the 8 fragment reads of the next slice
@@ -274,13 +290,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
         if constexpr (decltype(lds_n)::value > 0)
           __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, NBF - 1, 0);  // MFMA
       }
     };
     using DsRead = std::integral_constant<int, 0x100>;
     using AnyDs = std::integral_constant<int, 0x080>;
     using Two = std::integral_constant<int, 2>;
-    using Six = std::integral_constant<int, 6>;
+    using Six = std::integral_constant<int, (NAC + 8 + 4 + NBF + 3) / 4>;  // LDS writes + reads per MFMA group
     read_frags(st, 16, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 0);
     mma(0);
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NBF; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     lds_barrier();
@@ -347,17 +363,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     lds_barrier();  // every wave is done with the last stage
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + i * 32 + frow;
+      const int r = (BM == 256 ? wm * 128 : 0) + i * 32 + frow;
 #pragma unroll
-      for (int j = 0; j < (DUAL ? 2 : 4); ++j)
+      for (int j = 0; j < (DUAL ? NBF / 2 : NBF); ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = (DUAL ? wn * 64 : wn * 128) + j * 32 + 8 * q + 4 * half;
+          const int c = (BM == 256 ? (DUAL ? wn * 64 : wn * 128) : (DUAL ? wave * 32 : wave * 64)) + j * 32 + 8 * q +
+                        4 * half;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = acc[i][j][4 * q + e];
-            v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + 2][4 * q + e] : x;
+            v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + NBF / 2][4 * q + e] : x;
           }
           *reinterpret_cast<uint2*>(ot + r * OST + c) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -608,20 +625,23 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   }
   if (a.dtype == MOE_BF16) {
     const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
-    const int64_t m_tiles = (a.max_rows + BM - 1) / BM + std::min(a.G, a.max_rows);
+    const bool small = (int64_t)a.max_rows <= (int64_t)kSmallTileRowsPerGroup * a.G;
+    const int bm = small ? 128 : 256;
+    const int64_t m_tiles = (a.max_rows + bm - 1) / bm + std::min(a.G, a.max_rows);
     // persistent grid: one block per CU (the LDS stages take a CU), a multiple of
     // the 8 XCDs, no more than the tiles there can be
     const int64_t max_tiles = m_tiles * n_tiles;
     if (max_tiles <= 0) return hipSuccess;
     const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
-    if (dual)
-      hipLaunchKernelGGL(grouped_gemm_bf16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const uint16_t*)a.B0, (const uint16_t*)a.B1, (uint16_t*)a.C, n_tiles);
-    else
-      hipLaunchKernelGGL(grouped_gemm_bf16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const uint16_t*)a.B0, nullptr, (uint16_t*)a.C, n_tiles);
+#define MOE_TILED(D, M)                                                                                        \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, stream,         \
+                     (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
+                     (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles)
+    if (dual && small) MOE_TILED(true, 128);
+    else if (dual) MOE_TILED(true, 256);
+    else if (small) MOE_TILED(false, 128);
+    else MOE_TILED(false, 256);
+#undef MOE_TILED
   } else {
     const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;
     if (blocks <= 0) return hipSuccess;
