@@ -56,7 +56,7 @@ constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
 // Block tile rows: 256, or 128 when groups are small (at most kSmallTileRowsPerGroup
 // rows per group on average): a 256-row tile then holds mostly padding rows, and
 // a tile's time follows the bytes it streams (A rows + weight rows), not its MFMAs.
-constexpr int kSmallTileRowsPerGroup = 80;
+constexpr int kSmallTileRowsPerGroup = 112;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
