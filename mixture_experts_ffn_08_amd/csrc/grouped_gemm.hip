@@ -53,10 +53,13 @@ namespace {
 
 constexpr int BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
-// Block tile rows: 256, or 128 when groups are small (at most kSmallTileRowsPerGroup
-// rows per group on average): a 256-row tile then holds mostly padding rows, and
-// a tile's time follows the bytes it streams (A rows + weight rows), not its MFMAs.
+// Block tile rows by the average rows per group: 128 up to kSmallTileRowsPerGroup,
+// 192 up to kMidTileRowsPerGroup, else 256.  A tile's time follows the bytes it
+// streams (A rows + weight rows), not its MFMAs, so a tile mostly of padding rows
+// costs nearly what a full one does.  Thresholds measured on the Qwen3-30B-A3B
+// shape (T = 1024..3072): 192-row tiles up to 160 rows per group lost to 256.
 constexpr int kSmallTileRowsPerGroup = 112;
+constexpr int kMidTileRowsPerGroup = 144;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
@@ -129,10 +132,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
   constexpr int NAC = BM / 32;                   // A chunks per thread per K step
   // Wave layout.  BM = 256: the 4 waves as 2 x 2, each 128 rows x 128 B rows (dual:
-  // 64 gate rows and the same 64 up rows), 4 x 4 fragments of 32.  BM = 128: the 4
-  // waves split the B rows four ways, each 128 rows x 64 B rows (dual: 32 gate and
-  // the same 32 up rows), 4 x 2 fragments.
-  constexpr int NBF = BM == 256 ? 4 : 2;
+  // 64 gate rows and the same 64 up rows), 4 x 4 fragments of 32.  BM = 128 or 192:
+  // the 4 waves split the B rows four ways, each all BM rows x 64 B rows (dual: 32
+  // gate and the same 32 up rows), BM / 32 x 2 fragments.
+  static_assert(BM == 128 || BM == 192 || BM == 256, "block tile rows");
+  constexpr int NAF = BM == 256 ? 4 : BM / 32;  // A fragments per wave
+  constexpr int NBF = BM == 256 ? 4 : 2;        // B fragments per wave
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
   __shared__ TileScan scan;
 
@@ -233,12 +238,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[NAF][NBF];
   // Fragment offsets inside a stage: A rows wm*128 + 32 i; B rows per the layout above.
   const int frow = lane & 31, half = lane >> 5, fk = 8 * half;
-  int a_off[4], b_off[4];
+  int a_off[NAF], b_off[NBF];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_off[i] = ((BM == 256 ? wm * 128 : 0) + i * 32 + frow) * LDS_STRIDE + fk;
+  for (int i = 0; i < NAF; ++i) a_off[i] = ((BM == 256 ? wm * 128 : 0) + i * 32 + frow) * LDS_STRIDE + fk;
 #pragma unroll
   for (int j = 0; j < NBF; ++j) {
     // BM = 256, dual: fragments 0,1 = gate rows wn*64 + {0,32}; 2,3 = the same rows of up.
@@ -247,16 +252,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
                                : (DUAL ? j * (BN / 2) + wave * 32 : wave * 64 + j * 32);
     b_off[j] = (BM + brow + frow) * LDS_STRIDE + fk;
   }
-  bf16x8 fa[2][4], fb[2][4];
+  bf16x8 fa[2][NAF], fb[2][NBF];
   auto read_frags = [&](const uint16_t* st, int ks, int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[buf][i] = as_bf16x8(ld16(st + a_off[i] + ks));
+    for (int i = 0; i < NAF; ++i) fa[buf][i] = as_bf16x8(ld16(st + a_off[i] + ks));
 #pragma unroll
     for (int j = 0; j < NBF; ++j) fb[buf][j] = as_bf16x8(ld16(st + b_off[j] + ks));
   };
   auto mma = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NAF; ++i)
 #pragma unroll
       for (int j = 0; j < NBF; ++j) acc[i][j] = mfma32x32x16(fb[buf][j], fa[buf][i], acc[i][j]);
   };
@@ -290,13 +295,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
         if constexpr (decltype(lds_n)::value > 0)
           __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, NBF - 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, NAF * NBF / 4 - 1, 0);  // MFMA
       }
     };
     using DsRead = std::integral_constant<int, 0x100>;
     using AnyDs = std::integral_constant<int, 0x080>;
     using Two = std::integral_constant<int, 2>;
-    using Six = std::integral_constant<int, (NAC + 8 + 4 + NBF + 3) / 4>;  // LDS writes + reads per MFMA group
+    using Six = std::integral_constant<int, (NAC + 8 + NAF + NBF + 3) / 4>;  // LDS writes + reads per MFMA group
     read_frags(st, 16, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 0);
     mma(0);
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     lds_barrier();  // the stage memory is free (the previous tile's epilogue is done with it)
     store(R0{}, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NAF; ++i)
 #pragma unroll
       for (int j = 0; j < NBF; ++j)
 #pragma unroll
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     uint16_t* ot = lds;
     lds_barrier();  // every wave is done with the last stage
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NAF; ++i) {
       const int r = (BM == 256 ? wm * 128 : 0) + i * 32 + frow;
 #pragma unroll
       for (int j = 0; j < (DUAL ? NBF / 2 : NBF); ++j)
@@ -625,8 +630,8 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   }
   if (a.dtype == MOE_BF16) {
     const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
-    const bool small = (int64_t)a.max_rows <= (int64_t)kSmallTileRowsPerGroup * a.G;
-    const int bm = small ? 128 : 256;
+    const int64_t rows_per_group = (a.max_rows + a.G - 1) / a.G;  // ceiling of the average
+    const int bm = rows_per_group <= kSmallTileRowsPerGroup ? 128 : rows_per_group <= kMidTileRowsPerGroup ? 192 : 256;
     const int64_t m_tiles = (a.max_rows + bm - 1) / bm + std::min(a.G, a.max_rows);
     // persistent grid: one block per CU (the LDS stages take a CU), a multiple of
     // the 8 XCDs, no more than the tiles there can be
@@ -637,10 +642,13 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, stream,         \
                      (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
                      (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles)
-    if (dual && small) MOE_TILED(true, 128);
-    else if (dual) MOE_TILED(true, 256);
-    else if (small) MOE_TILED(false, 128);
-    else MOE_TILED(false, 256);
+    if (bm == 128) {
+      if (dual) MOE_TILED(true, 128); else MOE_TILED(false, 128);
+    } else if (bm == 192) {
+      if (dual) MOE_TILED(true, 192); else MOE_TILED(false, 192);
+    } else {
+      if (dual) MOE_TILED(true, 256); else MOE_TILED(false, 256);
+    }
 #undef MOE_TILED
   } else {
     const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;

@@ -314,6 +314,7 @@ def test_zero_tokens_is_a_no_op():
 @pytest.mark.parametrize("dtype,sizes", [
     ("bf16", [0, 1, 127, 128, 129, 300]),                      # 256-row tile kernel
     ("bf16", [0, 1, 63, 64, 65, 127, 128, 129, 3]),            # small groups: 128-row tiles
+    ("bf16", [0, 1, 191, 192, 193, 150, 128, 129, 64]),        # mid-size groups: 192-row tiles
     ("f32", [0, 1, 127, 128, 129, 300]),
     ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7]),  # few rows per group: skinny kernel,
                                                                 # two token tiles per weight pass
