@@ -271,7 +271,7 @@ def main():
         token_sweep(args.workload, [int(v) for v in args.sweep_tokens.split(",")], args.steps, args.warmup)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
