@@ -47,7 +47,7 @@ class ExpertCache:
         return None if sh is None else tuple(minp.as_f32(m, self.inp.shape.dtype) for m in sh)
 
 
-class GpuRun:
+class LayerRun:
     """Upload one layer, run it once through the C ABI, keep host copies."""
 
     def __init__(self, inp: minp.LayerInputs, device="cuda", gathered: bool = False):

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from mixture_experts_ffn_08_amd import inputs as minp
-from support import TOL, ExpertCache, GpuRun, check_dispatch, check_route, check_stats, host, log, oracle_route
+from support import TOL, ExpertCache, LayerRun, check_dispatch, check_route, check_stats, host, log, oracle_route
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def test_config_parity(name):
     rng = np.random.default_rng(1234)
     t0 = time.time()
     inp = minp.LayerInputs(shape, seed=0)
-    run = GpuRun(inp)
+    run = LayerRun(inp)
     try:
         out = run.run()
         b = run.bufs
