@@ -26,7 +26,11 @@
 //    conflict-free ds_read_b128.  Within a step, the fragments of the next 16-wide
 //    k slice are read while the current one is multiplied, and the step's global
 //    loads and LDS writes are spread between the MFMAs (one wave per SIMD: a wave
-//    stalled on issuing a burst of loads leaves its MFMA unit idle).
+//    stalled on issuing a burst of loads leaves its MFMA unit idle).  The LDS
+//    writes go evenly over the four slices (two chunk pairs each, the last pair of
+//    a stage written after the barrier of the step before): the LDS pipe then
+//    never has more queued than it serves in one slice's MFMA time, and waves
+//    stall less on issuing LDS instructions.
 //  * MFMA operands swapped (weights as the "A" input), so each lane's accumulators
 //    hold 4 consecutive output columns.  The epilogue applies SiLU(gate) * up in
 //    fp32, rounds to bf16 (v_cvt_pk_bf16_f32), stages the tile in LDS and stores
@@ -61,6 +65,12 @@ constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
 constexpr int kSmallTileRowsPerGroup = 112;
 constexpr int kMidTileRowsPerGroup = 144;
 constexpr int kXcds = 8;
+// A chunks among the chunk pairs [lo, hi) of a K step's copy, with NAC A chunks per
+// thread (pair i holds A chunk i when i < NAC, and B chunk i).
+template <int NAC>
+constexpr int a_chunks(int lo, int hi) {
+  return (NAC < hi ? NAC : hi) > lo ? (NAC < hi ? NAC : hi) - lo : 0;
+}
 
 __device__ __forceinline__ int clamp_off(int v, int max_rows) { return min(max(v, 0), max_rows); }
 
@@ -227,16 +237,20 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_part(set, k0, q);
   };
-  auto store = [&](auto set, int stage) {
+  // LDS writes of chunks i in [lo, hi) (A chunk i if i < NAC, and B chunk i), in
+  // the order load_part issued them.
+  auto store_range = [&](auto set, int stage, int lo, int hi) {
     constexpr int S = decltype(set)::value;
     uint16_t* sa = lds + stage * STAGE;
     uint16_t* sb = sa + BM * LDS_STRIDE;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if (i < lo || i >= hi) continue;
       if (i < NAC) st16(sa + (crow + 32 * i) * LDS_STRIDE + ccol, ra[S][i % NAC]);
       st16(sb + (crow + 32 * i) * LDS_STRIDE + ccol, rb[S][i]);
     }
   };
+  auto store = [&](auto set, int stage) { store_range(set, stage, 0, 8); };
 
   f32x16 acc[NAF][NBF];
   // Fragment offsets inside a stage: A rows wm*128 + 32 i; B rows per the layout above.
@@ -284,10 +298,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // The global loads and LDS traffic are spread over the MFMAs: a wave that
     // issued its 16 loads back to back would stall on the vector memory queue
     // with its MFMA unit idle.  Per k slice (fenced, so that fragment lifetimes
-    // stay one slice long): 4 loads and the 8 fragment reads of the next slice
-    // (third slice: also the 16 LDS writes of the next stage), each load or group
-    // of LDS operations followed by MFMAs.  The step's barrier sits before the
-    // last slice.
+    // stay one slice long): 4 loads, the 8 fragment reads of the next slice and
+    // 4 LDS writes, each load or group of LDS operations followed by MFMAs.  The
+    // step's barrier sits before the last slice.
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -301,22 +314,35 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     using DsRead = std::integral_constant<int, 0x100>;
     using AnyDs = std::integral_constant<int, 0x080>;
     using Two = std::integral_constant<int, 2>;
-    using Six = std::integral_constant<int, (NAC + 8 + NAF + NBF + 3) / 4>;  // LDS writes + reads per MFMA group
+    // LDS writes, two chunk pairs per slice: step kt+1's pairs 2..7 (register set
+    // Other, loaded in step kt-1) in the first three slices, and step kt+2's pairs
+    // 0 and 1 (this step's own set, loaded in the first slice) after the barrier,
+    // into this step's stage, which every wave has then finished reading.  Each
+    // load thus has three slices to land, and no slice asks more of the LDS than
+    // it serves in that slice's MFMA time.
+    constexpr int kW[4] = {2 + a_chunks<NAC>(2, 4), 2 + a_chunks<NAC>(4, 6), 2 + a_chunks<NAC>(6, 8),
+                           2 + a_chunks<NAC>(0, 2)};
+    using Ops0 = std::integral_constant<int, (NAF + NBF + kW[0] + 3) / 4>;  // LDS reads + writes per MFMA group
+    using Ops1 = std::integral_constant<int, (NAF + NBF + kW[1] + 3) / 4>;
+    using Ops2 = std::integral_constant<int, (NAF + NBF + kW[2] + 3) / 4>;
+    using Ops3 = std::integral_constant<int, (NAF + NBF + kW[3] + 3) / 4>;
     read_frags(st, 16, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 0);
+    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 2, 4);
     mma(0);
-    slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops0{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 32, 0);
     if constexpr (MODE == kFull) load_part(set, kn, 1);
+    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 4, 6);
     mma(1);
-    slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops1{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
     if constexpr (MODE == kFull) load_part(set, kn, 2);
-    if constexpr (MODE != kLast) store(Other{}, S ^ 1);
+    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 6, 8);
     mma(0);
-    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Six{}); else slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops2{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (MODE != kLast) {
       // Every wave has read its last fragments of this stage and written the next
@@ -325,9 +351,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       lds_barrier();
       read_frags(lds + (S ^ 1) * STAGE, 0, 0);
     }
-    if constexpr (MODE == kFull) load_part(set, kn, 3);
+    if constexpr (MODE == kFull) {
+      load_part(set, kn, 3);
+      store_range(set, S, 0, 2);
+    }
     mma(1);
-    slice_pattern(DsRead{}, std::integral_constant<int, MODE != kLast ? 2 : 0>{});
+    if constexpr (MODE == kFull) slice_pattern(AnyDs{}, Ops3{});
+    else slice_pattern(DsRead{}, std::integral_constant<int, MODE != kLast ? 2 : 0>{});
   };
 
   using Full = std::integral_constant<int, kFull>;
@@ -343,6 +373,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   for (;;) {
     lds_barrier();  // the stage memory is free (the previous tile's epilogue is done with it)
     store(R0{}, 0);
+    store_range(R1{}, 1, 0, 2);  // step 1's first pairs, as a step's last slice would have
 #pragma unroll
     for (int i = 0; i < NAF; ++i)
 #pragma unroll
