@@ -37,6 +37,12 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// SiLU(g) = g / (1 + e^-g) for outputs that are rounded to bf16: the hardware
+// reciprocal (v_rcp_f32, about 1 ulp) in place of a correctly rounded fp32
+// division, which compiles to a dozen instructions.  Large |g| stays exact in
+// the limit: e^-g = inf gives g * 0, e^-g = 0 gives g.
+__device__ __forceinline__ float silu_bf16out(float g) { return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)); }
+
 // 32x32 output, K = 16 per instruction.  Lane l supplies A row (l % 32) and B
 // column (l % 32), each with the 8 k values 8*(l/32) .. 8*(l/32)+7.
 // Accumulator element i of lane l is row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.

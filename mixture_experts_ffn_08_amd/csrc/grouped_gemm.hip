@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = acc[i][j][4 * q + e];
-            v[e] = DUAL ? __fdividef(x, 1.f + __expf(-x)) * acc[i][j + NBF / 2][4 * q + e] : x;
+            v[e] = DUAL ? silu_bf16out(x) * acc[i][j + NBF / 2][4 * q + e] : x;
           }
           *reinterpret_cast<uint2*>(ot + r * OST + c) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float x = acc[tt][0][i];
-            v[i] = __fdividef(x, 1.f + __expf(-x)) * acc[tt][1][i];
+            v[i] = silu_bf16out(x) * acc[tt][1][i];
           }
           *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         } else {
