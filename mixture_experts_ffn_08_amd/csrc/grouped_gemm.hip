@@ -61,9 +61,11 @@ constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
 // 192 up to kMidTileRowsPerGroup, else 256.  A tile's time follows the bytes it
 // streams (A rows + weight rows), not its MFMAs, so a tile mostly of padding rows
 // costs nearly what a full one does.  Thresholds measured on the Qwen3-30B-A3B
-// shape (T = 1024..3072): 192-row tiles up to 160 rows per group lost to 256.
-constexpr int kSmallTileRowsPerGroup = 112;
-constexpr int kMidTileRowsPerGroup = 144;
+// shape (E = 128, T = 1024..4096, each tile size forced in turn): 128-row tiles
+// win up to 100 rows per group and lose from 104, 192-row tiles win up to 156
+// and lose from 160 (groups of a few rows over the mean then need two tiles).
+constexpr int kSmallTileRowsPerGroup = 100;
+constexpr int kMidTileRowsPerGroup = 156;
 constexpr int kXcds = 8;
 // A chunks among the chunk pairs [lo, hi) of a K step's copy, with NAC A chunks per
 // thread (pair i holds A chunk i when i < NAC, and B chunk i).
