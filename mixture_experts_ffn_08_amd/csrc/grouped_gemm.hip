@@ -41,8 +41,10 @@
 //    in turn, and inside an expert the tiles run in bands of up to 8 m-tiles (down
 //    the band, then across n), so the tiles an XCD holds at once share their
 //    weight slices and their rows through that XCD's L2.
-//    The next tile's first two K steps are loaded while the current tile's output
-//    is stored.
+//    The last two K steps of a tile load the first two of the block's next tile,
+//    spread over their MFMAs like every other step's loads (issued as a burst in
+//    the epilogue they held the waves for a memory round trip), and the gather's
+//    row indices are fetched a tile ahead.
 //  * Global loads are buffer loads (scalar resource, 32-bit lane offset, the K
 //    offset as the scalar offset), which keeps 64-bit per-lane addresses out of the
 //    register budget.
@@ -156,6 +158,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   constexpr int NBF = BM == 256 ? 4 : 2;        // B fragments per wave
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
   __shared__ TileScan scan;
+  __shared__ int tile_rows[256];  // gather: row indices of the tile being set up
 
   const int total = scan_tiles<BM>(offsets, G, max_rows, scan) * n_tiles;
   // Persistent schedule.  Hardware block b runs on XCD b % 8 (blocks are dealt
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const uint32_t b_step = 32u * (uint32_t)K * 2u;
   int b_mask;
   int row0, row_end, n0;
+  int pre_row = 0;
   // B rows of a tile: dual -> gate rows [n0, n0+128) then up rows [n0, n0+128);
   // single -> rows [n0, n0+256), or [n0, n0+128) twice for a last tile of 128
   // columns (the columns past N are not stored).
@@ -209,17 +213,28 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
                    : rsrc_b0;
     b_mask = (DUAL || n0 + BN > N) ? 3 : 7;
     int arow[NAC];
+    if (a_rows != nullptr) {
+      // thread tid fetched the index of the tile's row tid; each thread needs those
+      // of its rows crow + 32 i
+      tile_rows[tid] = pre_row;
+      lds_barrier();
 #pragma unroll
-    for (int i = 0; i < NAC; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
-    if (a_rows != nullptr) {  // gather through the row index: all loads in flight, one wait
-      int v[NAC];
+      for (int i = 0; i < NAC; ++i) arow[i] = min(max(tile_rows[crow + 32 * i], 0), a_nrows - 1);
+    } else {
 #pragma unroll
-      for (int i = 0; i < NAC; ++i) v[i] = a_rows[arow[i]];
-#pragma unroll
-      for (int i = 0; i < NAC; ++i) arow[i] = min(max(v[i], 0), a_nrows - 1);
+      for (int i = 0; i < NAC; ++i) arow[i] = min(row0 + crow + 32 * i, row_end - 1);
     }
 #pragma unroll
     for (int i = 0; i < NAC; ++i) a_off8[i] = ((uint32_t)arow[i] * (uint32_t)K + ccol) * 2u;
+  };
+  // Gather: thread tid loads the row index of tile t's row tid, a tile ahead of
+  // setup(t), so that setup issues no load of its own (one register across the K
+  // loop; setup shares the indices through LDS).
+  auto fetch_rows = [&](int t) {
+    if (a_rows == nullptr) return;
+    int g, nt, r0, re;
+    locate<BM>(G, scan, n_tiles, t, g, r0, re, nt);
+    pre_row = a_rows[min(r0 + tid, re - 1)];
   };
 
   // Two register sets: the loads of K step kt+2 are issued while step kt is
@@ -289,17 +304,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   // Step kt: stage kt & 1 is in LDS, register set kt & 1 is free again, set
-  // (kt + 1) & 1 holds step kt+1 in flight.  Modes: kFull loads step kt+2 and
-  // stores step kt+1 to the other stage; kNoLoad (step nk-2) only stores; kLast
-  // (step nk-1) neither, and leaves the final barrier to the epilogue.  No step has
-  // a branch (a join would make the compiler's wait counts drain the loads just
-  // issued).
-  constexpr int kFull = 0, kNoLoad = 1, kLast = 2;
-  auto step = [&](auto set, int kt, auto mode) {
+  // (kt + 1) & 1 holds step kt+1 in flight.  Every step loads K offset kn into its
+  // own set: step kt+2 of this tile, or in the last two steps, steps 0 and 1 of
+  // the block's next tile (whose first stage is then in flight through this
+  // tile's epilogue, not issued as a burst in it).  Modes: kFull also stores step
+  // kt+1 to the other stage; kPre (step nk-2) stores but writes no pair of the
+  // next tile; kPreLast (step nk-1) stores nothing and leaves the final barrier to
+  // the epilogue.  No step has a branch (a join would make the compiler's wait
+  // counts drain the loads just issued).
+  constexpr int kFull = 0, kPre = 1, kPreLast = 2;
+  auto step = [&](auto set, int kn, auto mode) {
     constexpr int S = decltype(set)::value;
     constexpr int MODE = decltype(mode)::value;
     using Other = std::integral_constant<int, S ^ 1>;
-    const int kn = (kt + 2) * BK;
     const uint16_t* st = lds + S * STAGE;
     // The global loads and LDS traffic are spread over the MFMAs: a wave that
     // issued its 16 loads back to back would stall on the vector memory queue
@@ -310,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (MODE == kFull) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
         if constexpr (decltype(lds_n)::value > 0)
           __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
@@ -333,47 +350,51 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     using Ops2 = std::integral_constant<int, (NAF + NBF + kW[2] + 3) / 4>;
     using Ops3 = std::integral_constant<int, (NAF + NBF + kW[3] + 3) / 4>;
     read_frags(st, 16, 1);
-    if constexpr (MODE == kFull) load_part(set, kn, 0);
-    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 2, 4);
+    load_part(set, kn, 0);
+    if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 2, 4);
     mma(0);
-    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops0{}); else slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops0{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 32, 0);
-    if constexpr (MODE == kFull) load_part(set, kn, 1);
-    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 4, 6);
+    load_part(set, kn, 1);
+    if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 4, 6);
     mma(1);
-    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops1{}); else slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops1{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
-    if constexpr (MODE == kFull) load_part(set, kn, 2);
-    if constexpr (MODE != kLast) store_range(Other{}, S ^ 1, 6, 8);
+    load_part(set, kn, 2);
+    if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 6, 8);
     mma(0);
-    if constexpr (MODE != kLast) slice_pattern(AnyDs{}, Ops2{}); else slice_pattern(DsRead{}, Two{});
+    if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops2{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (MODE != kLast) {
+    if constexpr (MODE != kPreLast) {
       // Every wave has read its last fragments of this stage and written the next
       // one: after the barrier the next stage's first fragments are read while the
       // last slice is multiplied, so no wave waits on LDS at the step boundary.
       lds_barrier();
       read_frags(lds + (S ^ 1) * STAGE, 0, 0);
     }
-    if constexpr (MODE == kFull) {
-      load_part(set, kn, 3);
-      store_range(set, S, 0, 2);
-    }
+    load_part(set, kn, 3);
+    if constexpr (MODE == kFull) store_range(set, S, 0, 2);
     mma(1);
     if constexpr (MODE == kFull) slice_pattern(AnyDs{}, Ops3{});
-    else slice_pattern(DsRead{}, std::integral_constant<int, MODE != kLast ? 2 : 0>{});
+    else slice_pattern(DsRead{}, std::integral_constant<int, MODE != kPreLast ? 2 : 0>{});
   };
 
   using Full = std::integral_constant<int, kFull>;
-  using NoLoad = std::integral_constant<int, kNoLoad>;
-  using Last = std::integral_constant<int, kLast>;
+  using Pre = std::integral_constant<int, kPre>;
+  using PreLast = std::integral_constant<int, kPreLast>;
   constexpr int TN = DUAL ? BN / 2 : BN;  // output columns of a block tile
   constexpr int OST = TN + 8;             // bf16 per LDS output row
   static_assert(BM * OST <= 2 * STAGE, "output tile must fit in the stage memory");
 
+  // The row indices of the block's next tile are fetched before the operand
+  // loads of the steps that follow, so that the K loop's wait counts only see
+  // operand loads behind them (the block's last tile fetches its own again).
+  auto after = [&](int t) { return t + nslots < run_end ? t + nslots : t; };
+  fetch_rows(tile);
   setup(tile);
+  fetch_rows(after(tile));
   load(R0{}, 0);
   load(R1{}, BK);
   for (;;) {
@@ -389,11 +410,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     lds_barrier();
     read_frags(lds, 0, 0);
     for (int kt = 0; kt < nk - 2; kt += 2) {
-      step(R0{}, kt, Full{});
-      step(R1{}, kt + 1, Full{});
+      step(R0{}, (kt + 2) * BK, Full{});
+      step(R1{}, (kt + 3) * BK, Full{});
     }
-    step(R0{}, nk - 2, NoLoad{});
-    step(R1{}, nk - 1, Last{});
+    // The last two steps load the first two of the block's next tile (the last
+    // tile re-loads itself: no load sits under a branch).
+    const int e_row0 = row0, e_row_end = row_end, e_n0 = n0;
+    const int next = tile + nslots;
+    const bool more = next < run_end;
+    setup(more ? next : tile);
+    fetch_rows(after(more ? next : tile));
+    step(R0{}, 0, Pre{});
+    step(R1{}, BK, PreLast{});
 
     // Epilogue through LDS.  acc[i][j] element r of lane l: output row (m) = 32 i +
     // l % 32 of the wave's rows, output column (n) = 8 (r / 4) + 4 (l / 32) + r % 4 of
@@ -422,14 +450,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
     }
-    // The next tile's first two K steps are loaded while this tile's rows are
-    // stored (the block's last tile re-loads itself: no load sits under a branch).
-    const int e_row0 = row0, e_row_end = row_end, e_n0 = n0;
-    const int next = tile + nslots;
-    const bool more = next < run_end;
-    setup(more ? next : tile);
-    load(R0{}, 0);
-    load(R1{}, BK);
     lds_barrier();
     constexpr int CPR = TN / 8;  // 16-byte chunks per output row
     const int ncols = DUAL ? TN : min(TN, N - e_n0);
