@@ -451,13 +451,33 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
         }
     }
     lds_barrier();
-    constexpr int CPR = TN / 8;  // 16-byte chunks per output row
+    // Thread tid stores 16-byte chunk tid % CPR of rows tid / CPR + RSTEP u.  The
+    // stores are buffer stores whose range ends at the tile's last row of the
+    // group; a chunk past that row, or (single) past column N, lies beyond the
+    // range and is dropped, so the loop has no branch.  Its LDS reads go out in
+    // groups of 8 ahead of their stores: one read, wait and store at a time paid
+    // the LDS latency per chunk (about 5k cycles of a down tile's 128 KB).
+    constexpr int CPR = TN / 8;          // 16-byte chunks per output row
+    constexpr int RSTEP = 256 / CPR;     // rows between one thread's chunks
+    constexpr int NST = BM * CPR / 256;  // chunks per thread
     const int ncols = DUAL ? TN : min(TN, N - e_n0);
-#pragma unroll 4
-    for (int c = tid; c < BM * CPR; c += 256) {
-      const int r = c / CPR, cc = 8 * (c % CPR);
-      const int row = e_row0 + r;
-      if (row < e_row_end && cc < ncols) st16(C + (size_t)row * N + e_n0 + cc, ld16(ot + r * OST + cc));
+    const int e_rows = min(e_row_end - e_row0, BM);
+    const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(C + (size_t)e_row0 * N), (short)0, (int)((uint32_t)e_rows * (uint32_t)N * 2u), kBufferFlags);
+    const int sr = tid / CPR, sc = 8 * (tid % CPR);
+    const uint32_t c_off = sc < ncols ? ((uint32_t)sr * (uint32_t)N + (uint32_t)(e_n0 + sc)) * 2u : 0x80000000u;
+    const uint32_t c_step = (uint32_t)RSTEP * (uint32_t)N * 2u;
+    const uint16_t* os = ot + sr * OST + sc;
+#pragma unroll
+    for (int u0 = 0; u0 < NST; u0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u0 + u < NST) v[u] = ld16(os + (u0 + u) * RSTEP * OST);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u0 + u < NST)
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsrc_c, (int)(c_off + (uint32_t)(u0 + u) * c_step), 0, 0);
     }
     if (!more) break;
     tile = next;
