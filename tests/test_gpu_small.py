@@ -357,3 +357,47 @@ def test_grouped_gemm_hand_made_groups(dtype, sizes):
                             dev(wu), dev(wd), a2, y2)
     torch.cuda.synchronize()
     assert torch.equal(a2, a) and torch.equal(y2, y), "row-index gather must match the materialized rows"
+
+
+@pytest.mark.parametrize("d,F", [(128, 128), (256, 128), (128, 384)])
+def test_grouped_gemm_many_tiles_per_block(d, F):
+    """256-row tiles, several per block (more tiles than blocks), with K = 128 (the
+    tile's K loop is only its two next-tile steps), 256 and 384: each block's tile
+    boundaries, the next tile's operand loads issued in the last steps and the row
+    indices fetched a tile ahead.  Against the oracle, and the gathered form bit for
+    bit against the materialized one."""
+    rng = np.random.default_rng(11)
+    G = 64
+    sizes = rng.integers(900, 1400, size=G)
+    sizes[5] = 0
+    sizes[17] = 1
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    max_rows = int(offsets[-1]) + 5
+
+    def mk(shape, scale):
+        v = (rng.standard_normal(shape) * scale).astype(np.float32)
+        return minp.bf16_bits_to_f32(minp.f32_to_bf16_bits(v))
+
+    xp = mk((max_rows, d), 1.0)
+    wg, wu, wd = mk((G, F, d), d ** -0.5), mk((G, F, d), d ** -0.5), mk((G, d, F), F ** -0.5)
+    dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    a = torch.full((max_rows, F), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((max_rows, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    off = torch.from_numpy(offsets).cuda()
+    log(f"[many_tiles d={d} F={F}] {int(offsets[-1])} rows in {G} groups")
+    _lib.moe_grouped_swiglu(dev(xp), None, 0, off, G, max_rows, d, F, dev(wg), dev(wu), dev(wd), a, y)
+    torch.cuda.synchronize()
+    a_ref, y_ref = oracle.grouped_swiglu(xp, offsets, lambda e: (wg[e], wu[e], wd[e]))
+    R = int(offsets[-1])
+    assert max_rel(host(a)[:R], a_ref) <= TOL["bf16"]
+    assert max_rel(host(y)[:R], y_ref) <= TOL["bf16"]
+    assert (host(a)[R:] == 7.0).all() and (host(y)[R:] == 7.0).all(), "rows outside every group are untouched"
+    perm = rng.permutation(max_rows).astype(np.int32)
+    src = np.empty_like(xp)
+    src[perm] = xp
+    a2 = torch.full_like(a, 7.0)
+    y2 = torch.full_like(y, 7.0)
+    _lib.moe_grouped_swiglu(dev(src), torch.from_numpy(perm).cuda(), max_rows, off, G, max_rows, d, F, dev(wg),
+                            dev(wu), dev(wd), a2, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(a2, a) and torch.equal(y2, y), "row-index gather must match the materialized rows"
