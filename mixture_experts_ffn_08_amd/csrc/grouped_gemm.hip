@@ -13,9 +13,11 @@
 // bf16 kernel (gfx950):
 //  * 256 threads = 4 waves; block tile 256 rows x 256 B-rows (dual: 128 gate rows
 //    and the same 128 up rows, so one block produces 256 x 128 of SiLU*up);
-//    each wave owns 128 x 128 as 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators).
-//    A 256 x 256 tile is the smallest for which LDS reads + writes per K step stay
-//    under the MFMA time of the step with 4 waves.
+//    each wave owns 128 x 128 as 4 x 4 MFMA 32x32x16 tiles (256 fp32 accumulators,
+//    so one wave per SIMD).  The largest tile 4 waves can hold, it moves the fewest
+//    L2 and LDS bytes per MFMA: with one wave per SIMD the LDS serves about 126
+//    B/clk per CU (latency-bound; far more with more waves), and a K step's LDS
+//    reads and writes must fit in its MFMA time.
 //  * K step 64; global -> registers -> LDS, two LDS stages (147 KB) and two
 //    register sets: the 16-byte loads of step kt+2 are issued while step kt is
 //    multiplied, because under full load a global round trip takes longer than one
@@ -27,10 +29,11 @@
 //    k slice are read while the current one is multiplied, and the step's global
 //    loads and LDS writes are spread between the MFMAs (one wave per SIMD: a wave
 //    stalled on issuing a burst of loads leaves its MFMA unit idle).  The LDS
-//    writes go evenly over the four slices (two chunk pairs each, the last pair of
-//    a stage written after the barrier of the step before): the LDS pipe then
-//    never has more queued than it serves in one slice's MFMA time, and waves
-//    stall less on issuing LDS instructions.
+//    writes go evenly over the four slices, two chunk pairs each: a stage's first
+//    two pairs right after the barrier of the step that finished reading it, the
+//    other six in the next step's first three slices.  The LDS pipe then never
+//    has more queued than it serves in one slice's MFMA time, and waves stall
+//    less on issuing LDS instructions.
 //  * MFMA operands swapped (weights as the "A" input), so each lane's accumulators
 //    hold 4 consecutive output columns.  The epilogue applies SiLU(gate) * up in
 //    fp32, rounds to bf16 (v_cvt_pk_bf16_f32), stages the tile in LDS and stores
@@ -86,6 +89,19 @@ struct TileScan {
 
 // Block-wide: per-group m-tile counts, their inclusive prefix and the clamped group
 // bounds; returns the total.
+// The rest of a round of a k slice's pattern: its other MPR - 1 MFMAs, each
+// after its share of the round's N LDS operations (spread one or two at a time
+// between MFMAs rather than bunched after the first).
+template <int MASK, int N, int MPR, int S>
+__device__ __forceinline__ void lds_slots() {
+  if constexpr (S < MPR) {
+    constexpr int c = N / (MPR - 1) + (S <= N % (MPR - 1) ? 1 : 0);
+    if constexpr (c > 0) __builtin_amdgcn_sched_group_barrier(MASK, c, 0);  // LDS
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+    lds_slots<MASK, N, MPR, S + 1>();
+  }
+}
+
 template <int BM>
 __device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, TileScan& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -322,16 +338,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // issued its 16 loads back to back would stall on the vector memory queue
     // with its MFMA unit idle.  Per k slice (fenced, so that fragment lifetimes
     // stay one slice long): 4 loads, the 8 fragment reads of the next slice and
-    // 4 LDS writes, each load or group of LDS operations followed by MFMAs.  The
-    // step's barrier sits before the last slice.
+    // 4 LDS writes, in 4 rounds of a load and the round's MFMAs with its LDS
+    // operations one or two between each pair of MFMAs (bunched three at a time
+    // they ran about 1% slower).  The step's barrier sits before the last slice.
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                // MFMA
-        if constexpr (decltype(lds_n)::value > 0)
-          __builtin_amdgcn_sched_group_barrier(decltype(lds_mask)::value, decltype(lds_n)::value, 0);  // LDS
-        __builtin_amdgcn_sched_group_barrier(0x008, NAF * NBF / 4 - 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        lds_slots<decltype(lds_mask)::value, decltype(lds_n)::value, NAF * NBF / 4, 1>();
       }
     };
     using DsRead = std::integral_constant<int, 0x100>;
