@@ -115,19 +115,31 @@ def measured_copy_rate(torch, nbytes: int = 1 << 30) -> float:
     return rate
 
 
-def timed_steps(layer, x, bufs, steps, warmup, stream, torch):
+def timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=0.0):
     """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down).
     With large groups the balance statistics run on a second stream beside the
     combine (MoeLayer.forward); a step ends when both streams are done.  The timed
     steps record no events inside; the per-launch GEMM times come from as many
-    further steps with events around the two launches."""
+    further steps with events around the two launches.  min_warm_ms > 0 (the
+    sweeps): further warm-up steps until the warm-up has run that long, since the
+    part takes tens of milliseconds of load to reach its working clock and a
+    small layer's warm-up steps may not add up to that."""
     side = torch.cuda.Stream()
 
     def step(ev=None):
         layer.forward(x, bufs, stream, side_stream=side, marks=ev)
 
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0.record(stream)
     for _ in range(warmup):
         step()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    spent = w0.elapsed_time(w1)
+    if warmup > 0 and min_warm_ms > spent:
+        for _ in range(int(np.ceil((min_warm_ms - spent) / max(spent / warmup, 1e-3)))):
+            step()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -206,7 +218,7 @@ def config_sweep(steps: int, warmup: int):
         bufs = Buffers(shape, shape.T, "cuda:0")
         setup_s = time.time() - t0
         with torch.cuda.stream(stream):
-            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch)
+            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
         R = int(bufs.offsets[-1].item())
         touched = int((bufs.counts > 0).sum().item())
         s = shape
@@ -245,7 +257,7 @@ def token_sweep(name: str, tokens, steps: int, warmup: int):
         x = to_device(inp.x, s.dtype, "cuda:0")
         bufs = Buffers(s, T, "cuda:0")
         with torch.cuda.stream(stream):
-            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch)
+            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
         touched = int((bufs.counts > 0).sum().item())
         wbytes = touched * 3 * s.d * s.F * s.elem_bytes
         nbytes = wbytes + (s.E * s.d + 2 * T * s.d) * s.elem_bytes
