@@ -34,7 +34,9 @@
  *     check (expert ids, offsets) are clamped or skipped as stated per call.
  *
  * Limits: 1 <= k <= E <= 256.  d and F multiples of 8 (MOE_F32) or of 128
- * (MOE_BF16); other sizes return MOE_ERR_UNSUPPORTED.
+ * (MOE_BF16); other sizes return MOE_ERR_UNSUPPORTED.  The grouped GEMMs
+ * address each operand (x or a, one expert's weights) with 32-bit byte
+ * offsets: an operand over 4 GiB returns MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H
