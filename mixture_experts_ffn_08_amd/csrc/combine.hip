@@ -9,12 +9,22 @@
 // (no atomics) and summed in slot order in fp32, then rounded once: the result is
 // deterministic.  The loads of all k slots (and the shared row) for up to 4 chunks
 // are issued before any arithmetic, so a lane keeps up to 4 (k + 1) loads in
-// flight; k is a template parameter for the common values.
+// flight; k is a template parameter for the common values.  Every byte is read
+// or written once, so the loads and stores are non-temporal: with the default
+// policy the read-once rows took cache space to no use, and the combine ran at
+// 4.97 TB/s instead of 5.86 (qwen3 prefill shape, 121.6 vs 103.4 us).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
+
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 template <bool BF16>
 __device__ __forceinline__ void accumulate(float* acc, const u32x4 v, float w) {
@@ -74,8 +84,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       for (int u = 0; u < kChunksPerLane; ++u) {
         const size_t off = (size_t)min(c0 + 64 * u, chunks - 1) * 16;  // past the end: re-read, not stored
 #pragma unroll
-        for (int j = 0; j < KT; ++j) v[u][j] = ld16(src[j] + off);
-        if (SHARED) vs[u] = ld16(shrow + off);
+        for (int j = 0; j < KT; ++j) v[u][j] = ld16_nt(src[j] + off);
+        if (SHARED) vs[u] = ld16_nt(shrow + off);
       }
 #pragma unroll
       for (int u = 0; u < kChunksPerLane; ++u) {
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
         }
-        if (c < chunks) st16(yt + (size_t)c * 16, o);
+        if (c < chunks) st16_nt(yt + (size_t)c * 16, o);
       }
     }
   } else {
@@ -105,9 +115,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       for (int j = 0; j < k; ++j) {
         const int r = row_of[(size_t)t * k + j];
         if (r < 0 || r >= rows) continue;
-        accumulate<BF16>(acc, ld16(yp + (size_t)r * row_bytes + (size_t)c * 16), topk_w[(size_t)t * k + j]);
+        accumulate<BF16>(acc, ld16_nt(yp + (size_t)r * row_bytes + (size_t)c * 16), topk_w[(size_t)t * k + j]);
       }
-      if (SHARED) accumulate<BF16>(acc, ld16(sh + (size_t)t * row_bytes + (size_t)c * 16), 1.f);
+      if (SHARED) accumulate<BF16>(acc, ld16_nt(sh + (size_t)t * row_bytes + (size_t)c * 16), 1.f);
       u32x4 o;
       if (BF16) {
 #pragma unroll
@@ -116,7 +126,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
       }
-      st16(yt + (size_t)c * 16, o);
+      st16_nt(yt + (size_t)c * 16, o);
     }
   }
 }
