@@ -37,7 +37,11 @@
 //  * MFMA operands swapped (weights as the "A" input), so each lane's accumulators
 //    hold 4 consecutive output columns.  The epilogue applies SiLU(gate) * up in
 //    fp32, rounds to bf16 (v_cvt_pk_bf16_f32), stages the tile in LDS and stores
-//    whole rows.
+//    whole rows.  With K >= 256 the tile is staged in stage 1's memory (single: in
+//    two passes of 128 rows) while the next tile's step 0 goes to stage 0, so the
+//    loads of its step 2 can be issued before the output stores: gfx950 retires
+//    loads and stores through one in-order counter, and a load queued behind
+//    128 KB of stores cannot be waited for until they have been written.
 //  * Persistent: one block per CU.  Tiles of all groups are enumerated on the
 //    device from offsets (no host round trip); each XCD (blocks are dealt
 //    round-robin to the 8 XCDs) owns a contiguous run of tiles that its blocks take
@@ -158,7 +162,7 @@ __device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int
 }
 
 
-template <bool DUAL, int BM>
+template <bool DUAL, int BM, bool EARLY>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // next tile; kPreLast (step nk-1) stores nothing and leaves the final barrier to
   // the epilogue.  No step has a branch (a join would make the compiler's wait
   // counts drain the loads just issued).
-  constexpr int kFull = 0, kPre = 1, kPreLast = 2;
+  constexpr int kFull = 0, kPre = 1, kPreLast = 2, kFirst = 3;
   auto step = [&](auto set, int kn, auto mode) {
     constexpr int S = decltype(set)::value;
     constexpr int MODE = decltype(mode)::value;
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     auto slice_pattern = [&](auto lds_mask, auto lds_n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        if constexpr (MODE != kFirst) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         lds_slots<decltype(lds_mask)::value, decltype(lds_n)::value, NAF * NBF / 4, 1>();
       }
@@ -365,19 +369,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     using Ops2 = std::integral_constant<int, (NAF + NBF + kW[2] + 3) / 4>;
     using Ops3 = std::integral_constant<int, (NAF + NBF + kW[3] + 3) / 4>;
     read_frags(st, 16, 1);
-    load_part(set, kn, 0);
+    if constexpr (MODE != kFirst) load_part(set, kn, 0);
     if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 2, 4);
     mma(0);
     if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops0{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 32, 0);
-    load_part(set, kn, 1);
+    if constexpr (MODE != kFirst) load_part(set, kn, 1);
     if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 4, 6);
     mma(1);
     if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops1{}); else slice_pattern(DsRead{}, Two{});
     __builtin_amdgcn_sched_barrier(0);
     read_frags(st, 48, 1);
-    load_part(set, kn, 2);
+    if constexpr (MODE != kFirst) load_part(set, kn, 2);
     if constexpr (MODE != kPreLast) store_range(Other{}, S ^ 1, 6, 8);
     mma(0);
     if constexpr (MODE != kPreLast) slice_pattern(AnyDs{}, Ops2{}); else slice_pattern(DsRead{}, Two{});
@@ -389,19 +393,25 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       lds_barrier();
       read_frags(lds + (S ^ 1) * STAGE, 0, 0);
     }
-    load_part(set, kn, 3);
-    if constexpr (MODE == kFull) store_range(set, S, 0, 2);
+    if constexpr (MODE != kFirst) load_part(set, kn, 3);
+    if constexpr (MODE == kFull || MODE == kFirst) store_range(set, S, 0, 2);
     mma(1);
-    if constexpr (MODE == kFull) slice_pattern(AnyDs{}, Ops3{});
+    if constexpr (MODE == kFull || MODE == kFirst) slice_pattern(AnyDs{}, Ops3{});
     else slice_pattern(DsRead{}, std::integral_constant<int, MODE != kPreLast ? 2 : 0>{});
   };
 
   using Full = std::integral_constant<int, kFull>;
   using Pre = std::integral_constant<int, kPre>;
   using PreLast = std::integral_constant<int, kPreLast>;
+  using First = std::integral_constant<int, kFirst>;
   constexpr int TN = DUAL ? BN / 2 : BN;  // output columns of a block tile
   constexpr int OST = TN + 8;             // bf16 per LDS output row
-  static_assert(BM * OST <= 2 * STAGE, "output tile must fit in the stage memory");
+  // Output staging.  EARLY: the tile goes through stage 1's memory, in one pass
+  // (dual) or two passes of half the rows (single), while stage 0 takes the next
+  // tile's step 0; otherwise it takes both stages in one pass.
+  constexpr int PASSES = EARLY && !DUAL ? 2 : 1;
+  constexpr int PROWS = BM / PASSES;      // output rows per pass
+  static_assert(PROWS * OST <= (EARLY ? 1 : 2) * STAGE, "output tile must fit in the stage memory");
 
   // The row indices of the block's next tile are fetched before the operand
   // loads of the steps that follow, so that the K loop's wait counts only see
@@ -412,9 +422,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   fetch_rows(after(tile));
   load(R0{}, 0);
   load(R1{}, BK);
+  if constexpr (EARLY) {
+    // every tile starts with step 0 in stage 0 and step 2 in flight in set 0
+    store(R0{}, 0);
+    load(R0{}, 2 * BK);
+  }
   for (;;) {
     lds_barrier();  // the stage memory is free (the previous tile's epilogue is done with it)
-    store(R0{}, 0);
+    if constexpr (!EARLY) store(R0{}, 0);
     store_range(R1{}, 1, 0, 2);  // step 1's first pairs, as a step's last slice would have
 #pragma unroll
     for (int i = 0; i < NAF; ++i)
@@ -424,7 +439,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     lds_barrier();
     read_frags(lds, 0, 0);
-    for (int kt = 0; kt < nk - 2; kt += 2) {
+    if constexpr (EARLY) {
+      // step 2's loads went out before the previous tile's output stores (the
+      // vector memory counter retires in issue order, so a load issued behind
+      // the stores could not be waited for before they completed)
+      step(R0{}, 0, First{});
+      step(R1{}, 3 * BK, Full{});
+    }
+    for (int kt = EARLY ? 2 : 0; kt < nk - 2; kt += 2) {
       step(R0{}, (kt + 2) * BK, Full{});
       step(R1{}, (kt + 3) * BK, Full{});
     }
@@ -444,55 +466,84 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     // rows with 16 bytes apiece; instead the block's bf16 tile is written to LDS
     // (row-major, rows padded by 16 bytes) and then stored as whole rows, 16 bytes
     // per lane, so each instruction writes 8 full 128-byte lines.
-    uint16_t* ot = lds;
-    lds_barrier();  // every wave is done with the last stage
+    uint16_t* ot = EARLY ? lds + STAGE : lds;
+    // Pass p writes fragments [p NAF / PASSES, (p + 1) NAF / PASSES) of every wave
+    // to LDS: with two passes and BM = 256, tile rows [64 p, 64 p + 64) (waves
+    // wm = 0) and [128 + 64 p, 192 + 64 p) (wm = 1) as LDS rows 0..127; with BM <
+    // 256, tile rows [p PROWS, (p + 1) PROWS).
+    constexpr int FPP = NAF / PASSES;  // fragments per wave and pass
+    auto write_out = [&](auto pass) {
+      constexpr int P = decltype(pass)::value;
 #pragma unroll
-    for (int i = 0; i < NAF; ++i) {
-      const int r = (BM == 256 ? wm * 128 : 0) + i * 32 + frow;
+      for (int i = P * FPP; i < (P + 1) * FPP; ++i) {
+        const int r = (BM == 256 ? wm * (128 / PASSES) : 0) + (i - P * FPP) * 32 + frow;
 #pragma unroll
-      for (int j = 0; j < (DUAL ? NBF / 2 : NBF); ++j)
+        for (int j = 0; j < (DUAL ? NBF / 2 : NBF); ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = (BM == 256 ? (DUAL ? wn * 64 : wn * 128) : (DUAL ? wave * 32 : wave * 64)) + j * 32 + 8 * q +
-                        4 * half;
-          float v[4];
+          for (int q = 0; q < 4; ++q) {
+            const int c = (BM == 256 ? (DUAL ? wn * 64 : wn * 128) : (DUAL ? wave * 32 : wave * 64)) + j * 32 +
+                          8 * q + 4 * half;
+            float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = acc[i][j][4 * q + e];
-            v[e] = DUAL ? silu_bf16out(x) * acc[i][j + NBF / 2][4 * q + e] : x;
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[i][j][4 * q + e];
+              v[e] = DUAL ? silu_bf16out(x) * acc[i][j + NBF / 2][4 * q + e] : x;
+            }
+            *reinterpret_cast<uint2*>(ot + r * OST + c) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
           }
-          *reinterpret_cast<uint2*>(ot + r * OST + c) =
-              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        }
-    }
-    lds_barrier();
-    // Thread tid stores 16-byte chunk tid % CPR of rows tid / CPR + RSTEP u.  The
-    // stores are buffer stores whose range ends at the tile's last row of the
-    // group; a chunk past that row, or (single) past column N, lies beyond the
-    // range and is dropped, so the loop has no branch.  Its LDS reads go out in
-    // groups of 8 ahead of their stores: one read, wait and store at a time paid
-    // the LDS latency per chunk (about 5k cycles of a down tile's 128 KB).
-    constexpr int CPR = TN / 8;          // 16-byte chunks per output row
-    constexpr int RSTEP = 256 / CPR;     // rows between one thread's chunks
-    constexpr int NST = BM * CPR / 256;  // chunks per thread
+      }
+    };
+    // Thread tid stores 16-byte chunk tid % CPR of rows tid / CPR + RSTEP u of a
+    // pass.  The stores are buffer stores whose range ends at the tile's last row
+    // of the group; a chunk past that row, or (single) past column N, lies beyond
+    // the range and is dropped, so the loop has no branch.  Its LDS reads go out
+    // in groups of 8 ahead of their stores: one read, wait and store at a time
+    // paid the LDS latency per chunk (about 5k cycles of a down tile's 128 KB).
+    constexpr int CPR = TN / 8;             // 16-byte chunks per output row
+    constexpr int RSTEP = 256 / CPR;        // rows between one thread's chunks
+    constexpr int NST = PROWS * CPR / 256;  // chunks per thread and pass
     const int ncols = DUAL ? TN : min(TN, N - e_n0);
-    const int e_rows = min(e_row_end - e_row0, BM);
-    const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(C + (size_t)e_row0 * N), (short)0, (int)((uint32_t)e_rows * (uint32_t)N * 2u), kBufferFlags);
     const int sr = tid / CPR, sc = 8 * (tid % CPR);
     const uint32_t c_off = sc < ncols ? ((uint32_t)sr * (uint32_t)N + (uint32_t)(e_n0 + sc)) * 2u : 0x80000000u;
     const uint32_t c_step = (uint32_t)RSTEP * (uint32_t)N * 2u;
     const uint16_t* os = ot + sr * OST + sc;
+    const int e_rows = min(e_row_end - e_row0, BM);
+    const __amdgpu_buffer_rsrc_t rsrc_c = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(C + (size_t)e_row0 * N), (short)0, (int)((uint32_t)e_rows * (uint32_t)N * 2u), kBufferFlags);
+    // LDS row lr of pass p is tile row lr + p PROWS, or with two passes and BM = 256,
+    // 128 (lr / 64) + 64 p + lr % 64.
+    auto store_out = [&](auto pass) {
+      constexpr int P = decltype(pass)::value;
+      constexpr int HALF = 64 / RSTEP;  // chunks per thread in LDS rows 0..63
 #pragma unroll
-    for (int u0 = 0; u0 < NST; u0 += 8) {
-      u32x4 v[8];
+      for (int u0 = 0; u0 < NST; u0 += 8) {
+        u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (u0 + u < NST) v[u] = ld16(os + (u0 + u) * RSTEP * OST);
+        for (int u = 0; u < 8; ++u)
+          if (u0 + u < NST) v[u] = ld16(os + (u0 + u) * RSTEP * OST);
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (u0 + u < NST)
-          __builtin_amdgcn_raw_buffer_store_b128(v[u], rsrc_c, (int)(c_off + (uint32_t)(u0 + u) * c_step), 0, 0);
+        for (int u = 0; u < 8; ++u)
+          if (u0 + u < NST) {
+            const int trow = BM == 256 && PASSES == 2 ? 64 * P + ((u0 + u) >= HALF ? 64 : 0) : P * PROWS;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v[u], rsrc_c, (int)(c_off + (uint32_t)(u0 + u) * c_step + (uint32_t)trow * (uint32_t)N * 2u), 0, 0);
+          }
+      }
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    lds_barrier();  // every wave is done with the last stage
+    write_out(P0{});
+    if constexpr (EARLY) store(R0{}, 0);  // the next tile's step 0
+    lds_barrier();
+    if constexpr (EARLY) load(R0{}, 2 * BK);  // its step 2, ahead of the stores
+    store_out(P0{});
+    if constexpr (PASSES == 2) {
+      lds_barrier();  // every wave has read the first pass
+      write_out(P1{});
+      lds_barrier();
+      store_out(P1{});
     }
     if (!more) break;
     tile = next;
@@ -730,10 +781,19 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
     const int64_t max_tiles = m_tiles * n_tiles;
     if (max_tiles <= 0) return hipSuccess;
     const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
-#define MOE_TILED(D, M)                                                                                        \
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M>), dim3((unsigned)blocks), dim3(256), 0, stream,         \
+    // Step 2 of a tile can be loaded in the previous tile's epilogue when there is one (K >= 256).
+    const bool early = a.K >= 4 * BK;
+#define MOE_TILED_E(D, M, E)                                                                                   \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M, E>), dim3((unsigned)blocks), dim3(256), 0, stream,      \
                      (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
                      (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles)
+#define MOE_TILED(D, M)          \
+  do {                           \
+    if (early)                   \
+      MOE_TILED_E(D, M, true);   \
+    else                         \
+      MOE_TILED_E(D, M, false);  \
+  } while (0)
     if (bm == 128) {
       if (dual) MOE_TILED(true, 128); else MOE_TILED(false, 128);
     } else if (bm == 192) {
@@ -742,6 +802,7 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
       if (dual) MOE_TILED(true, 256); else MOE_TILED(false, 256);
     }
 #undef MOE_TILED
+#undef MOE_TILED_E
   } else {
     const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;
     if (blocks <= 0) return hipSuccess;
