@@ -428,7 +428,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     load(R0{}, 2 * BK);
   }
   for (;;) {
-    lds_barrier();  // the stage memory is free (the previous tile's epilogue is done with it)
+    // The stage memory is free (the previous tile's epilogue is done with it).
+    // EARLY: stage 0 already holds step 0, written before this barrier, which
+    // also makes it visible; step 1's first pairs go to stage 1 after it, and
+    // are read only after the barrier inside step 0.
+    lds_barrier();
     if constexpr (!EARLY) store(R0{}, 0);
     store_range(R1{}, 1, 0, 2);  // step 1's first pairs, as a step's last slice would have
 #pragma unroll
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       for (int j = 0; j < NBF; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    lds_barrier();
+    if constexpr (!EARLY) lds_barrier();
     read_frags(lds, 0, 0);
     if constexpr (EARLY) {
       // step 2's loads went out before the previous tile's output stores (the
