@@ -576,11 +576,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
   const int nblk_n = N / sk_bn(DUAL);
-  // Hardware block b runs on XCD b % 8; XCD x takes the contiguous run of logical
-  // blocks [x q + min(x, r), ..) (q = n / 8, r = n % 8), so each XCD streams one
-  // eighth of the weights, whose pages its own address translation then covers.
-  const int n = (int)gridDim.x, xq = n / kXcds, xr = n % kXcds, xx = (int)blockIdx.x % kXcds;
-  const int lb = xx * xq + min(xx, xr) + (int)blockIdx.x / kXcds;
+  // each XCD streams one contiguous eighth of the weights
+  const int lb = xcd_contiguous_block();
   const int g = lb / nblk_n, nb = lb % nblk_n;
   const int lo = clamp_off(offsets[g], max_rows), hi = clamp_off(offsets[g + 1], max_rows);
   if (hi <= lo) return;
