@@ -39,10 +39,11 @@ constexpr int kBufferFlags = 0x00020000;
 // [x q + min(x, r), ..) of the n blocks (q = n / 8, r = n % 8), so a kernel whose
 // blocks stream consecutive regions has each XCD stream one contiguous eighth:
 // its address translation then covers only those pages.
-__device__ __forceinline__ int xcd_contiguous_block() {
-  const int n = (int)gridDim.x, q = n >> 3, r = n & 7, x = (int)blockIdx.x & 7;
-  return x * q + min(x, r) + ((int)blockIdx.x >> 3);
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int q = n >> 3, r = n & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
 }
+__device__ __forceinline__ int xcd_contiguous_block() { return xcd_contiguous((int)blockIdx.x, (int)gridDim.x); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

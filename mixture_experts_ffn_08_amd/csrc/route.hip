@@ -238,11 +238,16 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
   uint16_t* ws = reinterpret_cast<uint16_t*>(smem);
   float* tile = reinterpret_cast<float*>(smem);
 
-  const int e0 = SELECT ? 0 : blockIdx.y * L::EP;  // first expert of the block
+  // Blocks in XCD-contiguous order (the hardware deals them round-robin in x-major
+  // order), with a token block's expert blocks next to each other: each XCD reads
+  // its own run of x, each row twice through its L2 rather than from two XCDs.
+  const int lb = xcd_contiguous((int)(blockIdx.x + blockIdx.y * gridDim.x), (int)(gridDim.x * gridDim.y));
+  const int tb = lb / (int)gridDim.y, eb = lb % (int)gridDim.y;
+  const int e0 = SELECT ? 0 : eb * L::EP;  // first expert of the block
   const int E = SELECT ? E_all : min(L::EP, E_all - e0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int kg = lane >> 4;
-  const int t0 = blockIdx.x * kTokens;
+  const int t0 = tb * kTokens;
   const int rows = min(kTokens, T - t0);
   const int nst = d / L::BK;  // d % 128 == 0
   // Buffer resources over the block's token rows and its experts' router rows;
