@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                        int y_rows, void* __restrict__ y) {
   constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   const int k = KT > 0 ? KT : k_rt;
-  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));
   if (t >= T) return;
   const int lane = threadIdx.x & 63;
   const int chunks = d / EPC;
@@ -131,9 +131,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   }
 }
 
+constexpr int kCombineOneWaveBelowT = 1024;
+
 template <bool BF16>
 hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
-  const dim3 grid((a.T + 3) / 4), block(256);
+  // One wave per token; four per block, or one when there are few tokens (decode),
+  // so that the tokens spread over as many CUs as there are.
+  const int waves = a.T < kCombineOneWaveBelowT ? 1 : 4;
+  const dim3 grid((a.T + waves - 1) / waves), block(64 * waves);
 #define MOE_COMBINE(KT)                                                                                       \
   do {                                                                                                        \
     if (a.shared_y != nullptr)                                                                                \
