@@ -481,6 +481,53 @@ def test_worst_case_imbalance_collapsed_top2(golden):
     assert 1.0 <= oracle.balance_stats(counts1, s1, 256, k, E, 0.01)[3] <= E / k
 
 
+def _stats_from_probs(probs, k, mode=oracle.SOFTMAX_THEN_TOPK):
+    """Route tokens whose router probabilities are `probs` (scores = ln p, so the
+    softmax over all experts gives p back) and return the oracle's statistics."""
+    probs = np.asarray(probs, np.float64)
+    T, E = probs.shape
+    s = np.log(probs).astype(np.float32)
+    idx, _ = oracle.top_k(oracle.selection_keys(s, mode), k)
+    counts, *_ = oracle.dispatch(idx, E, None)
+    return idx, oracle.balance_stats(counts, s, T, k, E, alpha=1.0)
+
+
+@pytest.mark.parametrize("mode", [oracle.SOFTMAX_THEN_TOPK, oracle.TOPK_THEN_SOFTMAX])
+def test_P_on_the_worked_example_as_one_token_batch(golden, mode):
+    """P_i is the mean over tokens of the softmax over all E experts (ML Interview
+    Notes load_balancing_loss; The Residual Stream listing's probs.mean(0)), in
+    every score mode.  One token with the worked example's probabilities: P is
+    those probabilities, f = (1/2, 1/2, 0, 0) and E sum f P = 1.6; dividing P by
+    T k would give 0.8, taking it from the renormalized weights 2.0."""
+    g = golden("balance_pi_rs.txt")
+    E, k = int(g["E"]), int(g["k"])
+    idx, (f, P, l_bal, _) = _stats_from_probs([g["probs"]], k, mode)
+    assert sorted(idx[0].tolist()) == [0, 1]
+    np.testing.assert_array_equal(f, np.array(g["f_expected"], np.float32))
+    np.testing.assert_allclose(P, g["P_expected"], rtol=1e-6)
+    assert l_bal == pytest.approx(g["balance_term_expected"], rel=1e-6)
+    for wrong in (g["balance_term_if_P_over_Tk"], g["balance_term_if_P_from_renormalized_weights"]):
+        assert abs(l_bal - wrong) > 0.1
+    assert E == len(P)
+
+
+def test_P_is_the_plain_mean_over_tokens_at_k2():
+    """Three tokens, k = 2, E = 4, probabilities chosen so that the three readings
+    of P differ.  Rows: (.5 .3 .15 .05) -> experts {0, 1}; (.05 .15 .3 .5) -> {3, 2};
+    (.1 .2 .3 .4) -> {3, 2}.  P = column means = (.65, .65, .75, .95) / 3;
+    counts (1, 1, 2, 2) of T k = 6, so f = (1/6, 1/6, 1/3, 1/3), and
+    E sum f P = 4 (1.3 / 18 + 3.4 / 18) = 47 / 45.  With P over T k the term is
+    47 / 90; with P from the renormalized weights ((.625 .375 0 0), (0 0 .375 .625),
+    (0 0 3/7 4/7)) it is 10 / 9."""
+    probs = [[0.5, 0.3, 0.15, 0.05], [0.05, 0.15, 0.3, 0.5], [0.1, 0.2, 0.3, 0.4]]
+    idx, (f, P, l_bal, mom) = _stats_from_probs(probs, 2)
+    assert [sorted(r) for r in idx.tolist()] == [[0, 1], [2, 3], [2, 3]]
+    np.testing.assert_array_equal(f, np.array([1, 1, 2, 2], np.float32) / np.float32(6))
+    np.testing.assert_allclose(P, np.array([0.65, 0.65, 0.75, 0.95]) / 3, rtol=1e-6)
+    assert l_bal == pytest.approx(47 / 45, rel=1e-6)
+    assert mom == np.float32(4 * 2) / np.float32(6)
+
+
 def test_f_is_bit_exact_float32_division():
     counts = np.array([3, 0, 7, 1, 1, 0, 2, 2], np.int32)
     f, *_ = oracle.balance_stats(counts, np.zeros((8, 8), np.float32), 8, 2, 8, 0.01)
