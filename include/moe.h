@@ -23,7 +23,14 @@
  *     (logits), gate weights and statistics are float32.  Accumulation is
  *     float32.  bfloat16 results are rounded to nearest, ties to even.
  *   - Weights are held (out_features, in_features), as torch.nn.Linear holds
- *     them: W_r[E][d]; per expert gate[F][d], up[F][d], down[d][F].
+ *     them: W_r[E][d]; per expert gate[F][d], up[F][d], down[d][F].  The
+ *     Residual Stream's MoE listing ("An MoE tiny GPT") stacks the expert
+ *     matrices the other way round, gate and up as (E, d, F) and down as
+ *     (E, F, d), and multiplies h @ gate[e]: a caller holding tensors in that
+ *     order transposes each expert's matrices once (torch:
+ *     gate.transpose(1, 2).contiguous(), the same for up and down) before
+ *     passing them here.  K-contiguous rows let both MFMA operands load as
+ *     16-byte vectors along the reduction.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
  *     synchronize the host.  Arguments are checked on the host before
  *     anything is enqueued; on a bad argument a negative moe_status is
@@ -253,7 +260,9 @@ int moe_grouped_swiglu(const void* x, const int32_t* row_index, int src_rows,
  * deterministic.  row_of values outside [0, y_rows) count as dropped.
  *
  *   y_perm   device [y_rows][d] dtype: T*k rows for the compact layout
- *            (moe_permute), E*C for the padded one (moe_permute_padded)
+ *            (moe_permute), E*C for the padded one (moe_permute_padded).
+ *            With y_rows = 0 every slot counts as dropped, no row is read and
+ *            y_perm may be NULL (y is then shared_y, or zeros).
  *   row_of   device [T][k] int32; topk_w device [T][k] float32;
  *   shared_y device [T][d] dtype or NULL;
  *   y        device [T][d] dtype out (every row written)

@@ -218,10 +218,12 @@ def moe_grouped_swiglu(x, row_index, src_rows, offsets, G, max_rows, d, F, w_gat
 
 
 def moe_combine(y_perm, row_of, topk_w, shared_y, T, k, d, y, stream=None, y_rows=None):
-    """y_rows: rows of y_perm (default T*k, the compact layout; E*C for the padded one)."""
+    """y_rows: rows of y_perm (default T*k, the compact layout; E*C for the padded one).
+    With y_rows = 0 no row is read and y_perm may be None."""
     dt = _dtype_code(y)
     rows = T * k if y_rows is None else int(y_rows)
-    args = (_dev(y_perm, "y_perm", y.dtype, rows * d), rows, _dev(row_of, "row_of", torch.int32, T * k),
+    args = (_dev(y_perm, "y_perm", y.dtype, rows * d, optional=rows == 0), rows,
+            _dev(row_of, "row_of", torch.int32, T * k),
             _dev(topk_w, "topk_w", torch.float32, T * k),
             _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), dt, T, k, d,
             _dev(y, "y", y.dtype, T * d), _stream(stream))

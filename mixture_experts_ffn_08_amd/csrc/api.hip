@@ -297,7 +297,7 @@ int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const flo
   if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
   CHECK(assignments_check(fn, T, k));
   if (T == 0) return ok();
-  NEED(y_perm, fn);
+  if (y_rows > 0) NEED(y_perm, fn);
   NEED(row_of, fn);
   NEED(topk_w, fn);
   NEED(y, fn);

@@ -64,9 +64,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   char* yt = static_cast<char*>(y) + (size_t)t * row_bytes;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if constexpr (KT > 0) {
-    // A dropped slot reads row 0 (y_perm has y_rows >= 1 rows when any slot is
-    // kept) and its values are replaced by zeros after the load: no load sits
-    // under a branch.
+    // A dropped slot reads row 0 (this form runs only with y_rows >= 1) and its
+    // values are replaced by zeros after the load: no load sits under a branch.
     const char* src[KT];
     float w[KT];
     bool kept[KT];
@@ -148,7 +147,9 @@ hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((combine_kernel<BF16, KT, false>), grid, block, 0, stream, a.y_perm, a.row_of,     \
                          a.topk_w, nullptr, a.T, a.k, a.d, a.y_rows, a.y);                                    \
   } while (0)
-  switch (a.k) {
+  // The fixed-k forms read row 0 for a dropped slot; with an empty y_perm
+  // (y_rows = 0: every slot dropped) the runtime-k form runs, which reads no row.
+  switch (a.y_rows > 0 ? a.k : 0) {
     case 1: MOE_COMBINE(1); break;
     case 2: MOE_COMBINE(2); break;
     case 4: MOE_COMBINE(4); break;

@@ -87,10 +87,12 @@ def check_route(inp, out, ref=None, select_bias=None):
     """Scores within fp32 tolerance.  Selection runs on keys (the scores, their
     sigmoid, or with a selection bias softmax/score/sigmoid + b).  Outside
     near-tie tokens (k-th and (k+1)-th keys closer than the gap, on either side)
-    the chosen expert set is exact; the slot order is exact where consecutive
-    chosen keys are farther apart than the gap, and elsewhere follows the
-    kernel's own keys (descending, up to their rounding); gate weights, matched by
-    expert, within tolerance.  Returns the tokens whose chosen set may differ."""
+    the chosen expert set is exact; the slot order is exact except inside runs of
+    chosen keys that are consecutively closer than the gap, where the same
+    experts must fill the run's slots and their order follows the kernel's own
+    keys (descending, up to their rounding); gate weights, matched by expert,
+    within tolerance.  Logs how many tokens such runs exempt.  Returns the tokens
+    whose chosen set may differ."""
     s = inp.shape
     sb = inp.select_bias if select_bias is None else select_bias
     scores, idx, w, near = ref if ref is not None else oracle_route(inp, sb)
@@ -101,9 +103,17 @@ def check_route(inp, out, ref=None, select_bias=None):
     assert np.array_equal(np.sort(out["idx"][ok], 1), np.sort(idx[ok], 1)), "expert sets differ outside near ties"
     keys = oracle.selection_keys(scores, s.mode, sb).astype(np.float64)
     top = -np.sort(-keys, axis=1)[:, :s.k]
-    order_tie = (top[:, :-1] - top[:, 1:] < oracle.NEAR_TIE_GAP).any(1)
-    strict = ok & ~order_tie
-    assert np.array_equal(out["idx"][strict], idx[strict]), "slot order differs where the keys are well apart"
+    # Slot order: the chosen keys of a token fall into runs in which consecutive
+    # keys are closer than the gap; each run must hold the same experts on both
+    # sides, in the same slots as a set (order free only inside a run).
+    close = top[:, :-1] - top[:, 1:] < oracle.NEAR_TIE_GAP
+    run = np.concatenate([np.zeros((s.T, 1), np.int64), np.cumsum(~close, axis=1)], axis=1)[ok]
+    by_run = lambda i: np.sort(run * 4096 + i.astype(np.int64), axis=1)
+    assert np.array_equal(by_run(out["idx"][ok]), by_run(idx[ok][:, :s.k])), \
+        "slot order differs beyond runs of near-equal keys"
+    reordered = int((out["idx"][ok] != idx[ok]).any(1).sum())
+    close_tokens = int(close[ok].any(1).sum())
+    assert reordered <= close_tokens
     own_keys = oracle.selection_keys(out["scores"], s.mode, sb).astype(np.float64)
     own = np.take_along_axis(own_keys, out["idx"].astype(np.int64), 1)
     slack = 0.0 if (sb is None and s.mode != oracle.SIGMOID_THEN_TOPK) else 1e-6
@@ -118,7 +128,9 @@ def check_route(inp, out, ref=None, select_bias=None):
         diff = out["near_tie"] != near
         assert np.all(np.abs(gap[diff] - oracle.NEAR_TIE_GAP) < 1e-5)
     log(f"[{s.name}] route ok: {int(tie.sum())} near-tie tokens of {s.T}, "
-        f"{int((out['idx'] != idx).any(1).sum())} with different experts")
+        f"{int((out['idx'] != idx).any(1).sum())} with a different slot list; outside near ties "
+        f"{close_tokens} tokens hold chosen keys closer than the gap, {reordered} of them ordered "
+        f"differently inside such a run")
     return tie
 
 

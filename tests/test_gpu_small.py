@@ -401,3 +401,41 @@ def test_grouped_gemm_many_tiles_per_block(d, F):
                             dev(wu), dev(wd), a2, y2)
     torch.cuda.synchronize()
     assert torch.equal(a2, a) and torch.equal(y2, y), "row-index gather must match the materialized rows"
+
+
+@pytest.mark.parametrize("dtype,shared", [("bf16", True), ("bf16", False), ("f32", True)])
+@pytest.mark.parametrize("k", [2, 3, 8])
+def test_combine_with_every_slot_dropped_reads_no_row(dtype, shared, k):
+    """y_rows = 0 (an empty y_perm, every slot dropped): the combine reads no row
+    of y_perm, which may be absent, and y is the shared expert's output (or 0)."""
+    T, d = 37, 256
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(5)
+    sh = torch.randn(T, d, generator=g).to(td).cuda() if shared else None
+    row_of = torch.full((T, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.rand(T, k, generator=g).cuda()
+    y = torch.full((T, d), float("nan"), dtype=td, device="cuda")
+    _lib.moe_combine(None, row_of, w, sh, T, k, d, y, y_rows=0)
+    torch.cuda.synchronize()
+    want = host(sh) if shared else np.zeros((T, d), np.float32)
+    assert np.array_equal(host(y), want)
+    log(f"[combine empty y_perm {dtype} k={k} shared={shared}] y equals the shared rows exactly")
+
+
+def test_stats_on_the_worked_example_as_one_token_batch(golden):
+    """moe_stats straight against the pages: one token whose router probabilities
+    are The Residual Stream's worked example (scores ln p), k = 2 of 4 experts.
+    P = the printed probabilities, f = (1/2, 1/2, 0, 0), E sum f P = 1.6."""
+    g = golden("balance_pi_rs.txt")
+    E, k = int(g["E"]), int(g["k"])
+    logits = torch.from_numpy(np.log(np.array([g["probs"]], np.float64)).astype(np.float32)).cuda()
+    counts = torch.tensor([1, 1, 0, 0], dtype=torch.int32, device="cuda")
+    f, P = torch.empty(E, device="cuda"), torch.empty(E, device="cuda")
+    l_aux, mom = torch.empty(1, device="cuda"), torch.empty(1, device="cuda")
+    ws = torch.empty(max(_lib.moe_stats_workspace_bytes(1, E), 1), dtype=torch.uint8, device="cuda")
+    _lib.moe_stats(counts, logits, 1, k, E, 1.0, f, P, l_aux, mom, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(f), np.array(g["f_expected"], np.float32))
+    np.testing.assert_allclose(host(P), g["P_expected"], rtol=1e-6)
+    assert host(l_aux)[0] == pytest.approx(g["balance_term_expected"], rel=1e-6)
+    assert host(mom)[0] == 2.0
