@@ -191,6 +191,31 @@ int moe_permute_padded(const int32_t* topk_idx, int T, int k, int E, int64_t cap
 size_t moe_permute_workspace_bytes(int T, int k, int E);
 
 /*
+ * moe_permute_noalloc -- moe_permute with no workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments, results and
+ * errors as moe_permute (same kernels, bit-identical results).
+ *
+ * The scratch moe_permute takes as `workspace` lives instead in one
+ * MOE_NOALLOC_SCRATCH_BYTES array in the library's device memory, one copy per
+ * GPU, held from the library's load until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree); its first call on a device looks up that
+ * device's copy (hipGetSymbolAddress) with the device current.
+ *   - Sizes whose moe_permute_workspace_bytes(T, k, E) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES (4 MiB: T*k up to 2^20 assignments at E = 256,
+ *     2^21 at E = 128) return MOE_ERR_UNSUPPORTED before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last call's
+ *     contents; each call writes every word it reads first, so nothing needs
+ *     clearing.  Calls that overlap on one GPU (different streams, or host
+ *     threads) race on the array and must be ordered by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int64_t capacity,
+                        const void* x, int dtype, int d,
+                        int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token,
+                        void* x_perm, hipStream_t stream);
+
+/*
  * moe_capacity -- C = ceil(phi * k * T / E), evaluated exactly on the binary
  * value of phi (Transformers & Math 17.5 equation; Understanding Data,
  * "Capacity").  Returns -1 (dropless) when phi is not finite or negative, or

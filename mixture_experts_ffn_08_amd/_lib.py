@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX_THEN_TOPK, MOE_TOPK_THEN_SOFTMAX, MOE_SIGMOID_THEN_TOPK = 0, 1, 2
 MOE_MAX_EXPERTS = 256
 
-EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_padded", "moe_permute_workspace_bytes", "moe_capacity",
+EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_noalloc", "moe_permute_padded",
+           "moe_permute_workspace_bytes", "moe_capacity",
            "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
            "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
 
@@ -33,6 +34,7 @@ _SIGS = {
     "moe_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_bias_update": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P]),
     "moe_permute": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_permute_noalloc": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_permute_padded": (_I, [_P, _I, _I, _I, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_permute_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_capacity": (_I64, [_I64, _I, _I, ctypes.c_double]),
@@ -164,6 +166,19 @@ def moe_permute(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm
             _dev(x_perm, "x_perm", x.dtype, T * k * d, optional=True),
             _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     _check("moe_permute", load().moe_permute(*args))
+
+
+def moe_permute_noalloc(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, perm_token, x_perm,
+                        stream=None):
+    """moe_permute without a workspace: the library's own per-device scratch array
+    (MOE_NOALLOC_SCRATCH_BYTES) holds the per-block histograms."""
+    dt = _dtype_code(x)
+    args = (_dev(topk_idx, "topk_idx", torch.int32, T * k), T, k, E, int(capacity),
+            _dev(x, "x", x.dtype, T * d), dt, d, _dev(counts, "counts", torch.int32, E),
+            _dev(offsets, "offsets", torch.int32, E + 1), _dev(row_of, "row_of", torch.int32, T * k),
+            _dev(perm_token, "perm_token", torch.int32, T * k),
+            _dev(x_perm, "x_perm", x.dtype, T * k * d, optional=True), _stream(stream))
+    _check("moe_permute_noalloc", load().moe_permute_noalloc(*args))
 
 
 def moe_permute_padded(topk_idx, T, k, E, capacity, x, d, counts, offsets, row_of, slot_token, x_slots,

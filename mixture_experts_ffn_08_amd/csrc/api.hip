@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "kernels.h"
@@ -164,23 +165,44 @@ int moe_bias_update(const int32_t* counts, int T, int k, int E, float rate, floa
   return hip_status(moe::launch_bias_update(counts, T, k, E, rate, select_bias, stream), fn);
 }
 
-int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
-                int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token, void* x_perm,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  static const char* fn = "moe_permute";
+}  // extern "C"
+
+namespace {
+
+// Checks of moe_permute and moe_permute_noalloc on everything but the workspace:
+// the sizes first (T = 0 is then a valid no-op), then the pointers.
+int permute_size_check(const char* fn, int T, int k, int E, int dtype, int d) {
   if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
   if (!dtype_ok(dtype)) return fail(MOE_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
   CHECK(experts_check(fn, E, k));
   if (d <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: d = %d must be positive", fn, d);
   if (d % 8 != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d must be a multiple of 8", fn, d);
   CHECK(assignments_check(fn, T, k));
-  if (T == 0) return ok();
+  return MOE_OK;
+}
+
+int permute_pointer_check(const char* fn, const int32_t* topk_idx, const void* x, int32_t* counts,
+                          int32_t* offsets, int32_t* row_of, int32_t* perm_token, void* x_perm) {
   NEED(topk_idx, fn);
   NEED(counts, fn);
   NEED(offsets, fn);
   NEED(row_of, fn);
   NEED(perm_token, fn);
   if (x_perm != nullptr) NEED(x, fn);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
+                int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token, void* x_perm,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "moe_permute";
+  CHECK(permute_size_check(fn, T, k, E, dtype, d));
+  if (T == 0) return ok();
+  CHECK(permute_pointer_check(fn, topk_idx, x, counts, offsets, row_of, perm_token, x_perm));
   const size_t need = moe_permute_workspace_bytes(T, k, E);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
@@ -189,6 +211,69 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, 
   moe::PermuteArgs a{topk_idx, T, k, E, capacity < 0 ? -1 : capacity, x, d * elem_bytes(dtype), counts,
                      offsets, row_of, perm_token, x_perm, static_cast<int32_t*>(workspace),
                      reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + half), 0};
+  return hip_status(moe::launch_permute(a, stream), fn);
+}
+
+}  // extern "C"
+
+// Scratch of moe_permute_noalloc: the per-block expert histograms and running
+// bases that moe_permute keeps in its workspace argument.  One copy per device,
+// held from the library's load until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device, with that device current).
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev,
+                  r != hipSuccess ? hipGetErrorString(r) : "null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_permute_noalloc(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, const void* x, int dtype,
+                        int d, int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* perm_token,
+                        void* x_perm, hipStream_t stream) {
+  static const char* fn = "moe_permute_noalloc";
+  CHECK(permute_size_check(fn, T, k, E, dtype, d));
+  if (T == 0) return ok();
+  CHECK(permute_pointer_check(fn, topk_idx, x, counts, offsets, row_of, perm_token, x_perm));
+  const size_t need = moe_permute_workspace_bytes(T, k, E);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "%s: T = %d, k = %d, E = %d need %zu bytes of scratch, more than the %zu this entry point "
+                "holds; call moe_permute with a workspace instead",
+                fn, T, k, E, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(scratch_address(fn, &ws));
+  // Every scratch word the kernels read is written earlier in the same call (the
+  // histograms by hist_kernel, the bases by scan_kernel): nothing needs clearing.
+  const size_t half = need / 2;
+  moe::PermuteArgs a{topk_idx, T, k, E, capacity < 0 ? -1 : capacity, x, d * elem_bytes(dtype), counts,
+                     offsets, row_of, perm_token, x_perm, static_cast<int32_t*>(ws),
+                     reinterpret_cast<int32_t*>(static_cast<char*>(ws) + half), 0};
   return hip_status(moe::launch_permute(a, stream), fn);
 }
 

@@ -175,3 +175,15 @@ def test_combine_and_stats_reject_before_launch():
     assert lib.moe_stats(FAKE, FAKE, 4, 9, 8, 0.01, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert lib.moe_stats(FAKE, FAKE, 4, 2, 8, float("nan"), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert lib.moe_stats(None, None, 0, 2, 8, 0.01, None, None, None, None, None, 0, None) == 0
+
+
+def test_permute_noalloc_rejects_beyond_its_scratch_before_launch():
+    """moe_permute_noalloc refuses sizes whose scratch exceeds its fixed array, on the
+    host, before anything runs (the pointers are never dereferenced)."""
+    lib = _lib.load()
+    T, k, E = 1 << 18, 8, 256
+    assert _lib.moe_permute_workspace_bytes(T, k, E) > (4 << 20)
+    assert lib.moe_permute_noalloc(8, T, k, E, -1, 0, _lib.MOE_BF16, 128, 8, 8, 8, 8, 0, 0) == _lib.MOE_ERR_UNSUPPORTED
+    assert "scratch" in _lib.last_error()
+    assert lib.moe_permute_noalloc(8, 0, k, E, -1, 0, _lib.MOE_BF16, 128, 8, 8, 8, 8, 0, 0) == _lib.MOE_OK
+    assert lib.moe_permute_noalloc(0, 16, k, E, -1, 0, _lib.MOE_BF16, 128, 8, 8, 8, 8, 0, 0) == _lib.MOE_ERR_INVALID_ARG
