@@ -116,7 +116,8 @@ def measured_copy_rate(torch, nbytes: int = 1 << 30) -> float:
 
 
 def timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=0.0):
-    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up and down).
+    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up, down and
+    the shared expert (0 without one)).
     With large groups the balance statistics run on a second stream beside the
     combine (MoeLayer.forward); a step ends when both streams are done.  The timed
     steps record no events inside; the per-launch GEMM times come from as many
@@ -148,26 +149,30 @@ def timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=0.0):
     end.record(stream)
     torch.cuda.synchronize()
     total = start.elapsed_time(end)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     gu = [e[0].elapsed_time(e[1]) for e in evs]
     dn = [e[1].elapsed_time(e[2]) for e in evs]
-    return total / steps, float(np.mean(gu)), float(np.mean(dn))
+    sh = [e[2].elapsed_time(e[3]) for e in evs]
+    return total / steps, float(np.mean(gu)), float(np.mean(dn)), float(np.mean(sh))
 
 
 def cpu_baseline(inp, target_s):
     """The oracle, as it stands, on a growing prefix of the workload's tokens until
-    it has run for about target_s seconds; tokens/s of the last sample."""
+    it has run for about target_s seconds; tokens/s of the last sample, with the
+    oracle's own per-step wall times.  `cores` is the number of threads the oracle
+    ran on (its matrix products run in the BLAS library's thread pool; the rest
+    is one thread); `cpu_count` is what the operating system reports."""
     import oracle
     from mixture_experts_ffn_08_amd import inputs as minp
 
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        blas = 1
     s = inp.shape
     ex = {}
 
@@ -185,16 +190,75 @@ def cpu_baseline(inp, target_s):
     n, elapsed = 64, 0.0
     while True:
         n = min(n, s.T)
+        stages = {}
         t0 = time.perf_counter()
         oracle.layer_forward(xs[:n], wr, inp.bias, weights, sh, k=s.k, mode=s.mode, renorm=s.renorm, phi=s.phi,
-                             alpha=s.alpha, dtype=s.dtype)
+                             alpha=s.alpha, dtype=s.dtype, timings=stages)
         elapsed = time.perf_counter() - t0
         if elapsed >= target_s or n == s.T:
             break
         n = int(n * min(8.0, max(1.5, 1.1 * target_s / max(elapsed, 1e-3))))
-    return {"value": n / elapsed, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {n} of {s.T} tokens of the {s.name} layer, full oracle forward (float64), "
-                      f"{elapsed:.1f} s"}
+    return {"value": n / elapsed, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens of the {s.name} layer, the whole oracle forward "
+                      f"(float64 products of the bf16 values, numpy/BLAS), {elapsed:.1f} s",
+            "cpu_count": os.cpu_count(), "blas_threads": int(blas),
+            "stage_s": {k: round(v, 4) for k, v in stages.items()}}
+
+
+def ep_share(weights, x, bufs, shape, stream, torch, gpus: int = 8, phi: float = 1.25, steps: int = 20):
+    """One GPU's share of the layer under expert parallelism over `gpus` GPUs: the
+    first E / gpus experts, each with C = ceil(phi k T / E) slots of the
+    capacity-padded layout (the fixed-size buffers an all-to-all exchange would
+    deliver; the exchange itself is not run).  Rows are the dispatch of the
+    layer's own routing (bufs.topk_idx); the GEMMs run over all G C slots,
+    padding included.  Returns the gate/up and down launch times and their MFMA
+    fractions, counting either the kept rows or every slot."""
+    from mixture_experts_ffn_08_amd import _lib
+    s = shape
+    C = _lib.moe_capacity(s.T, s.k, s.E, phi)
+    G = s.E // gpus
+    dev = x.device
+    i32 = torch.int32
+    counts = torch.empty(s.E, dtype=i32, device=dev)
+    offsets = torch.empty(s.E + 1, dtype=i32, device=dev)
+    row_of = torch.empty((s.T, s.k), dtype=i32, device=dev)
+    slot_token = torch.empty(s.E * C, dtype=i32, device=dev)
+    x_slots = torch.empty((s.E * C, s.d), dtype=x.dtype, device=dev)
+    ws = torch.empty(max(_lib.moe_permute_workspace_bytes(s.T, s.k, s.E), 1), dtype=torch.uint8, device=dev)
+    _lib.moe_permute_padded(bufs.topk_idx, s.T, s.k, s.E, C, x, s.d, counts, offsets, row_of, slot_token, x_slots,
+                            ws, stream)
+    rows = G * C
+    xs, off = x_slots[:rows], offsets[:G + 1]
+    a = torch.empty((rows, s.F), dtype=x.dtype, device=dev)
+    y = torch.empty((rows, s.d), dtype=x.dtype, device=dev)
+    gate, up, down = weights.gate[:G], weights.up[:G], weights.down[:G]
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        _lib.moe_grouped_gate_up(xs, None, 0, off, G, rows, s.d, s.F, gate, up, a, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        _lib.moe_grouped_down(a, off, G, rows, s.F, s.d, down, y, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(steps):
+        run()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        run(e)
+    torch.cuda.synchronize()
+    gu = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dn = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    kept = int(torch.clamp(counts[:G], max=C).sum().item())
+    f_kept, f_all = 6.0 * kept * s.d * s.F, 6.0 * rows * s.d * s.F
+    t = (gu + dn) * 1e-3
+    return {"workload": f"{s.name} expert-parallel share: experts 0..{G - 1} of {s.E} ({gpus} GPUs), "
+                        f"capacity-padded layout, C = {C} (phi = {phi})",
+            "experts": G, "capacity": C, "slots": rows, "kept_rows": kept, "gate_up_ms": gu, "down_ms": dn,
+            "tflops_all_slots": f_all / t / 1e12, "frac_of_mfma_peak_all_slots": f_all / t / PEAK_BF16_FLOPS,
+            "tflops_kept_rows": f_kept / t / 1e12, "frac_of_mfma_peak_kept_rows": f_kept / t / PEAK_BF16_FLOPS}
 
 
 def config_sweep(steps: int, warmup: int):
@@ -218,16 +282,23 @@ def config_sweep(steps: int, warmup: int):
         bufs = Buffers(shape, shape.T, "cuda:0")
         setup_s = time.time() - t0
         with torch.cuda.stream(stream):
-            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
+            ms, gu_ms, dn_ms, sh_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
         R = int(bufs.offsets[-1].item())
         touched = int((bufs.counts > 0).sum().item())
         s = shape
-        flops = 6.0 * R * s.d * s.F + 6.0 * s.T * s.d * s.F_shared + 2.0 * s.T * s.d * s.E
+        routed_flops = 6.0 * R * s.d * s.F
+        shared_flops = 6.0 * s.T * s.d * s.F_shared
+        flops = routed_flops + shared_flops + 2.0 * s.T * s.d * s.E
         nbytes = (touched * 3 * s.d * s.F + 3 * s.d * s.F_shared + s.E * s.d + 2 * s.T * s.d) * s.elem_bytes
         print(json.dumps({
             "workload": name, "T": s.T, "d": s.d, "E": s.E, "k": s.k, "F": s.F, "F_shared": s.F_shared,
             "capacity_factor": s.phi, "ms_per_step": ms, "tokens_per_s": s.T / (ms * 1e-3),
-            "gate_up_ms": gu_ms, "down_ms": dn_ms, "kept_assignments": R, "experts_touched": touched,
+            "gate_up_ms": gu_ms, "down_ms": dn_ms,
+            "routed_gemm_frac_of_mfma_peak": routed_flops / ((gu_ms + dn_ms) * 1e-3) / PEAK_BF16_FLOPS,
+            "shared_ms": sh_ms if s.F_shared else None,
+            "shared_tflops": shared_flops / (sh_ms * 1e-3) / 1e12 if s.F_shared else None,
+            "shared_frac_of_mfma_peak": shared_flops / (sh_ms * 1e-3) / PEAK_BF16_FLOPS if s.F_shared else None,
+            "kept_assignments": R, "experts_touched": touched,
             "max_over_mean": float(bufs.max_over_mean.item()),
             "layer_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_mfma_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / PEAK_HBM_BYTES,
@@ -257,7 +328,7 @@ def token_sweep(name: str, tokens, steps: int, warmup: int):
         x = to_device(inp.x, s.dtype, "cuda:0")
         bufs = Buffers(s, T, "cuda:0")
         with torch.cuda.stream(stream):
-            ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
+            ms, gu_ms, dn_ms, _ = timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=150.0)
         touched = int((bufs.counts > 0).sum().item())
         wbytes = touched * 3 * s.d * s.F * s.elem_bytes
         nbytes = wbytes + (s.E * s.d + 2 * T * s.d) * s.elem_bytes
@@ -300,7 +371,7 @@ def main():
     bufs = Buffers(shape, shape.T, "cuda:0")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        ms, gu_ms, dn_ms = timed_steps(layer, x, bufs, args.steps, args.warmup, stream, torch)
+        ms, gu_ms, dn_ms, _ = timed_steps(layer, x, bufs, args.steps, args.warmup, stream, torch)
     R = int(bufs.offsets[-1].item())
     flops_gu = 4.0 * R * shape.d * shape.F
     flops_dn = 2.0 * R * shape.F * shape.d
@@ -328,6 +399,9 @@ def main():
                          "frac_of_mfma_peak": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / PEAK_BF16_FLOPS,
                          "down_ms": dn_ms},
     }
+    # one GPU's share under expert parallelism, on the same weights and routing
+    with torch.cuda.stream(stream):
+        result["ep_share"] = ep_share(weights, x, bufs, shape, stream, torch)
     # decode regime on the same weights
     if args.decode_workload:
         dshape = minp.SHAPES[args.decode_workload]
@@ -338,7 +412,7 @@ def main():
         dx = to_device(dinp.x, dshape.dtype, "cuda:0")
         dbufs = Buffers(dshape, dshape.T, "cuda:0")
         with torch.cuda.stream(stream):
-            dms, _, _ = timed_steps(dlayer, dx, dbufs, max(args.steps, 50), args.warmup, stream, torch)
+            dms, _, _, _ = timed_steps(dlayer, dx, dbufs, max(args.steps, 50), args.warmup, stream, torch)
         touched = int((dbufs.counts > 0).sum().item())
         dbytes = (touched * 3 * dshape.d * dshape.F + dshape.E * dshape.d + 2 * dshape.T * dshape.d) * 2
         copy_rate = measured_copy_rate(torch)

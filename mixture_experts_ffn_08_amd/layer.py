@@ -189,7 +189,8 @@ class MoeLayer:
         Small groups (decode) keep them on `stream`: there the fork and join cost
         more than the overlap saves.  Results are identical either way.
         marks: three events recorded on `stream` before gate/up, between gate/up
-        and down, and after down (for timing)."""
+        and down, and after down (for timing); a fourth, if given, after the
+        shared expert."""
         if b is None:
             b = self.buffers(x.shape[0])
         if b.T == 0:
@@ -209,6 +210,8 @@ class MoeLayer:
         if marks is not None:
             marks[2].record(st)
         self.shared_expert(x, b, st)
+        if marks is not None and len(marks) > 3:
+            marks[3].record(st)
         if side_stream is not None:
             self._fork_stats(b, st, side_stream)
         self.combine(b, st)

@@ -385,26 +385,45 @@ def balance_stats(counts, scores, T: int, k: int, E: int, alpha: float):
 # Whole layer.
 
 def layer_forward(x, w_router, bias, expert_weights, shared_weights, *, k: int, mode: int,
-                  renorm: bool, phi: Optional[float], alpha: float, dtype: str, select_bias=None):
+                  renorm: bool, phi: Optional[float], alpha: float, dtype: str, select_bias=None,
+                  timings: Optional[dict] = None):
     """The full layer, step by step, returning every intermediate.
 
     x, w_router: stored values (float32 arrays).  expert_weights(e) ->
     (gate[F][d], up[F][d], down[d][F]); shared_weights: the same triple or None.
-    dtype: "bf16" or "f32", the output storage type of y."""
+    dtype: "bf16" or "f32", the output storage type of y.
+    timings: if a dict is given, the wall seconds of each step are stored in it
+    (route, dispatch, experts, shared_expert, combine, stats)."""
+    import time
+    clock = [time.perf_counter()]
+
+    def lap(name):
+        now = time.perf_counter()
+        if timings is not None:
+            timings[name] = now - clock[0]
+        clock[0] = now
+
     x = np.asarray(x, np.float32)
     T = x.shape[0]
     E = np.asarray(w_router).shape[0]
     s, idx, w, near = route(x, w_router, bias, k, mode, renorm, select_bias)
+    lap("route")
     cap = capacity(T, k, E, phi)
     counts, offsets, row_of, perm_token = dispatch(idx, E, cap)
     x_perm = permute_rows(x, perm_token)
+    lap("dispatch")
     a, y_perm = grouped_swiglu(x_perm, offsets, expert_weights)
+    lap("experts")
     shared = None if shared_weights is None else swiglu(x, *shared_weights)
+    lap("shared_expert")
     y64 = combine(y_perm, row_of, w, shared, d=x.shape[1])
+    y = round_to(y64, dtype)
+    lap("combine")
     f, P, l_aux, mom = balance_stats(counts, s, T, k, E, alpha)
+    lap("stats")
     return dict(scores=s, idx=idx, w=w, near_tie=near, capacity=cap, counts=counts,
                 offsets=offsets, row_of=row_of, perm_token=perm_token, x_perm=x_perm,
-                a=a, y_perm=y_perm, shared=shared, y64=y64, y=round_to(y64, dtype),
+                a=a, y_perm=y_perm, shared=shared, y64=y64, y=y,
                 f=f, P=P, l_aux=l_aux, max_over_mean=mom)
 
 
