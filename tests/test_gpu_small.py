@@ -312,7 +312,8 @@ def test_zero_tokens_is_a_no_op():
 
 
 @pytest.mark.parametrize("dtype,sizes", [
-    ("bf16", [0, 1, 127, 128, 129, 300]),                      # 256-row tile kernel
+    ("bf16", [0, 1, 255, 256, 257, 600, 513, 170]),            # 256-row tiles (K = 256 and 384)
+    ("bf16", [0, 1, 127, 128, 129, 300]),                      # 192-row tiles
     ("bf16", [0, 1, 63, 64, 65, 127, 128, 129, 3]),            # small groups: 128-row tiles
     ("bf16", [0, 1, 191, 192, 193, 150, 128, 129, 64]),        # mid-size groups: 192-row tiles
     ("f32", [0, 1, 127, 128, 129, 300]),
@@ -359,13 +360,14 @@ def test_grouped_gemm_hand_made_groups(dtype, sizes):
     assert torch.equal(a2, a) and torch.equal(y2, y), "row-index gather must match the materialized rows"
 
 
-@pytest.mark.parametrize("d,F", [(128, 128), (256, 128), (128, 384)])
+@pytest.mark.parametrize("d,F", [(128, 128), (256, 128), (128, 384), (256, 256), (384, 512)])
 def test_grouped_gemm_many_tiles_per_block(d, F):
     """256-row tiles, several per block (more tiles than blocks), with K = 128 (the
-    tile's K loop is only its two next-tile steps), 256 and 384: each block's tile
-    boundaries, the next tile's operand loads issued in the last steps and the row
-    indices fetched a tile ahead.  Against the oracle, and the gathered form bit for
-    bit against the materialized one."""
+    tile's K loop is only its two next-tile steps), 256, 384 and 512 (the step-2
+    loads ahead of the output stores; 384 columns also end in a 128-column n-tile):
+    each block's tile boundaries, the next tile's operand loads issued in the last
+    steps and the row indices fetched a tile ahead.  Against the oracle, and the
+    gathered form bit for bit against the materialized one."""
     rng = np.random.default_rng(11)
     G = 64
     sizes = rng.integers(900, 1400, size=G)
