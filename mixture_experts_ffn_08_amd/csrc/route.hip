@@ -44,6 +44,9 @@ constexpr int kTokens = 64;   // tokens per block of the fused kernel
 #ifndef MOE_ROUTE_SPLIT_MAX_T
 #define MOE_ROUTE_SPLIT_MAX_T 2048
 #endif
+#ifndef MOE_ROUTE_GEMM
+#define MOE_ROUTE_GEMM 1
+#endif
 constexpr int kSplitWaves = 8;    // waves per block of the split score kernel
 constexpr int kSplitTile = 16;    // tokens and experts per block of the split score kernel
 constexpr int kSelectTokens = 16; // tokens per block of the select kernel
@@ -383,6 +386,126 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
                                 topk_w, near_tie);
 }
 
+// Scores as a GEMM with DMA-fed LDS stages, then selection, for many tokens and
+// 64 < E <= 128.  Block: 32 tokens and every expert; two blocks per CU, so that
+// one block's selection (serial DPP rounds) overlaps the other's loads.  Wave w
+// multiplies experts 32 w .. 32 w + 31 against the 32 tokens (32x32x16 MFMA,
+// router rows as the "A" operand), so an x byte is read from HBM once.
+//  * Each K step of 64 loads the block's 32 x rows and E router rows (128 bytes
+//    each: whole lines) straight into LDS (buffer_load_dwordx4 ... lds writes
+//    lane l's 16 bytes at M0 + 16 l), three stages deep; each stage is its own
+//    __shared__ array, so the compiler waits only for the DMA a read needs.
+//    16-byte chunk c of LDS row r sits at position c ^ ((r & 7) ^ ((r >> 3) & 1)):
+//    conflict-free fragment reads.
+//  * The score tile then takes stage 0's memory.
+//  * Measured (qwen3 shape, router alone, x in cache): T = 16384 28.4 us against
+//    35.9 for the register-operand scores and the separate selection; T = 2304
+//    17.7 vs 20.7.  64 tokens a block (one per CU) ran 32-33 us: its four
+//    selection passes did not overlap anything.  A six-deep x ring beside a
+//    three-deep router ring ran slower (31.4 us).
+constexpr int kGemmTokens = 32;
+constexpr int kGemmStages = 3;
+__device__ __forceinline__ int route_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+typedef __attribute__((address_space(3))) void* route_lds_t;
+
+template <int SPL>
+__global__ __launch_bounds__(256, 2) void route_gemm_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
+    float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ near_tie) {
+  constexpr int EP = 128, BK = 64, TT = kGemmTokens;
+  constexpr int STAGE = (TT + EP) * BK;  // bf16: 32 x rows, then 128 router rows (20 KB)
+  constexpr int TSTR = EP + 4;           // score tile stride (floats)
+  static_assert(TT * TSTR * 4 <= STAGE * 2, "the score tile fits in a stage");
+  __shared__ __attribute__((aligned(1024))) uint16_t s0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t s1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t s2[STAGE];
+
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int t0 = blockIdx.x * TT;
+  const int rows = min(TT, T - t0);
+  const int nst = d / BK;
+  const int nsteps = (nst + kGemmStages - 1) / kGemmStages * kGemmStages;  // padded with zero steps
+  // over the block's token rows only (32-bit offsets whatever T is)
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (size_t)t0 * d), (short)0, (int)((uint32_t)rows * (uint32_t)d * 2u), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wr, (short)0, (int)((uint32_t)E * (uint32_t)d * 2u), kBufferFlags);
+  constexpr uint32_t kOut = 0x80000000u;  // past every resource: reads zeros
+
+  // DMA: a step is 4 x instructions (8 rows each) and 16 router instructions;
+  // wave w issues x instruction w and router instructions 4w .. 4w + 3.  Lane l:
+  // row 8 j + l / 8 of instruction j, position l % 8, global chunk
+  // (l % 8) ^ (l / 8) ^ (j & 1).
+  const int c0 = (lane & 7) ^ (lane >> 3);
+  const uint32_t xo =
+      ((uint32_t)min(8 * wave + (lane >> 3), rows - 1) * (uint32_t)d + 8u * (c0 ^ (wave & 1))) * 2u;
+  uint32_t wo[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = 4 * wave + u;
+    const int n = 8 * j + (lane >> 3);
+    wo[u] = n < E ? ((uint32_t)n * (uint32_t)d + 8u * (c0 ^ (j & 1))) * 2u : kOut;
+  }
+  // step s loads K offset 64 min(s, nst - 1); the padding steps past nst read zeros
+  auto dma = [&](uint16_t* st, int s) __attribute__((always_inline)) {
+    const int kb = 2 * BK * min(s, nst - 1);
+    const uint32_t pad = s < nst ? 0u : kOut;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (route_lds_t)(st + 8 * wave * BK), 16, xo | pad, kb, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (route_lds_t)(st + (TT + 8 * (4 * wave + u)) * BK), 16,
+                                               wo[u] | pad, kb, 0, 0);
+  };
+  // Fragments: lane l reads row l % 32 of a 32-row block, chunk 2 ks + l / 32.
+  const int frow = lane & 31, fsw = route_swz(frow);
+  f32x16 acc = f32x16{};
+  auto compute = [&](const uint16_t* st) __attribute__((always_inline)) {
+    bf16x8 wf[4], xf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int pos = 8 * ((2 * ks + (lane >> 5)) ^ fsw);
+      wf[ks] = as_bf16x8(ld16(st + (TT + 32 * wave + frow) * BK + pos));
+      xf[ks] = as_bf16x8(ld16(st + frow * BK + pos));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma32x32x16(wf[ks], xf[ks], acc);
+  };
+  // Step s in stage `cur`: this wave's DMA of the stage has landed (the compiler
+  // waits for it before the read below), then every wave's has and every wave
+  // has finished the previous stage, which takes the DMA of step s + 2.
+  auto step = [&](uint16_t* cur, uint16_t* prev, int s) __attribute__((always_inline)) {
+    const uint32_t probe = *reinterpret_cast<const uint32_t*>(cur + lane * 2);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"v"(probe) : "memory");
+    dma(prev, s + kGemmStages - 1);
+    compute(cur);
+  };
+  dma(s0, 0);
+  dma(s1, 1);
+  for (int s = 0; s < nsteps; s += kGemmStages) {
+    step(s0, s2, s);
+    step(s1, s0, s + 1);
+    step(s2, s1, s + 2);
+  }
+  // the padding DMAs (zeros, past the last step) land, and every wave is done
+  // with the stages, before stage 0 takes the score tile
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  float* tile = reinterpret_cast<float*>(s0);
+  // accumulator element e of lane l: expert 32 w + 8 (e / 4) + 4 (l / 32) + e % 4,
+  // token l % 32
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int n = 32 * wave + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+    const float b = (bias != nullptr && n < E) ? bias[n] : 0.f;
+    tile[frow * TSTR + n] = acc[e] + b;
+  }
+  __syncthreads();
+  select_tile<8, SPL, TT / 16, true>(tile, TSTR, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx, topk_w,
+                                      near_tie);
+}
+
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
 // experts 16 j .. 16 j + 15.  MFMA 16x16x32 with operands loaded straight from
 // global memory: in k-step s of a 128-wide slice of d, lane group q (lanes
@@ -489,6 +612,12 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((route_select_kernel<NB, SPL>), dim3((a.T + kSelectTokens - 1) / kSelectTokens), block, 0,
                        stream, a.T, a.E, a.k, a.mode, a.renorm, a.select_bias, a.logits, a.topk_idx, a.topk_w,
                        a.near_tie);
+  } else if (a.dtype == MOE_BF16 && NB == 8 && MOE_ROUTE_GEMM) {
+    // 64 < E <= 128: scores as a DMA-fed GEMM, selection in the same block
+    hipLaunchKernelGGL((route_gemm_kernel<SPL>), dim3((a.T + kGemmTokens - 1) / kGemmTokens), block, 0, stream,
+                       (const uint16_t*)a.x,
+                       (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
+                       a.logits, a.topk_idx, a.topk_w, a.near_tie);
   } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
              (int64_t)a.T * ((a.E + kScoreSplitExperts - 1) / kScoreSplitExperts) <= kScoreSplitMaxRowReads) {
     // many experts: 64-expert score blocks (two per CU), then selection; each block

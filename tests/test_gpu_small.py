@@ -50,6 +50,13 @@ SMALL = [
     S("many_tokens_softmax_biased", "bf16", 2100, 128, 64, 6, 128, 0, SM_TK, False, None, False,
       select_bias=0.01),
     S("f32_sigmoid_biased", "f32", 100, 72, 5, 2, 40, 0, SIG, False, None, False, select_bias=0.1),
+    # 64 < E <= 128 above the few-token threshold: scores as a DMA-fed GEMM with the selection in
+    # the same block; each score mode, a selection bias and a logit bias, d / 64 not a multiple of 3
+    S("many_tokens_E96_sigmoid_biased", "bf16", 2100, 256, 96, 6, 128, 0, SIG, False, None, False,
+      select_bias=0.05),
+    S("many_tokens_E128_topk_first_zipf", "bf16", 2300, 384, 128, 8, 128, 0, TK_SM, False, None, True),
+    S("many_tokens_E72_softmax_biased", "bf16", 2051, 1152, 72, 8, 128, 0, SM_TK, False, None, False,
+      select_bias=0.01),
     # E = 256 with T (E / 64) past the split-score limit: the fused kernel with 256 experts
     S("many_tokens_E256_fused", "bf16", 8300, 128, 256, 8, 128, 0, SM_TK, True, None, True, select_bias=0.002),
 ]
