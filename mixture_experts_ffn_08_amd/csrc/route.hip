@@ -75,35 +75,34 @@ struct RouteLds {
   static constexpr int kBytes = kTileBytes > kWsBytes ? kTileBytes : kWsBytes;
 };
 
-// a beats b: larger key, or equal key and lower expert index.
-__device__ __forceinline__ bool beats(uint32_t ao, uint32_t ai, uint32_t bo, uint32_t bi) {
-  return ao > bo || (ao == bo && ai < bi);
-}
-
-// One butterfly step of the row arg-max; the winner's value bv travels with it.
+// Row arg-max step over packed candidates: the order key in the upper 32 bits and
+// the complemented expert index in the lower, so that one unsigned compare puts
+// the larger key first and, between equal keys, the lower index.
 template <int CTRL>
-__device__ __forceinline__ void argmax_step(uint32_t& bo, uint32_t& bi, float& bv) {
-  const uint32_t oo = dpp<CTRL>(bo), oi = dpp<CTRL>(bi);
-  const float ov = __uint_as_float(dpp<CTRL>(__float_as_uint(bv)));
-  if (beats(oo, oi, bo, bi)) { bo = oo; bi = oi; bv = ov; }
+__device__ __forceinline__ void pmax_step(uint64_t& best) {
+  const uint64_t o = ((uint64_t)dpp<CTRL>((uint32_t)(best >> 32)) << 32) | dpp<CTRL>((uint32_t)best);
+  best = o > best ? o : best;
 }
 
-// Top-k for 16 * PASSES tokens of a score tile (LDS, or the score rows in global
-// memory).  Each pass gives every 16-lane row of the 4 waves one token: tile row
-// 16 pass + 4 wave + row.  NB keys per lane; SPL result slots per lane (slot j
-// lives in lane j % 16, register j / 16).  WRITE_SCORES copies the tile rows to
-// the score output.
+// Top-k for 4 NW PASSES tokens of a score tile (LDS, or the score rows in global
+// memory).  Each pass gives every 16-lane row of the NW waves one token: tile row
+// 4 NW pass + 4 wave + row.  NB keys per lane (lane r of a row holds experts
+// r + 16 i); SPL result slots per lane (slot j lives in lane j % 16, register
+// j / 16).  WRITE_SCORES copies the tile rows to the score output.
 //
-// Each expert has a base value, which its weight is built from, and a selection
-// key (the base plus the selection bias when there is one):
-//   softmax then top-k:  base e = exp(s - max s); key s, or e / z + b
-//   top-k then softmax:  base s;                  key s, or s + b
-//   sigmoid then top-k:  base g = 1 / (1 + exp(-s)); key g, or g + b
-// The arg-max carries the winner's base; the weights are then e / z (e / sum of
-// the chosen e with renorm), the softmax of the chosen s (an online maximum: with
-// a bias the first winner need not have the largest score), or g / sum of the
-// chosen g.
-template <int NB, int SPL, int PASSES, bool WRITE_SCORES>
+// Selection keys: the score s, or with a selection bias b, softmax(s) + b
+// (softmax then top-k), s + b (top-k then softmax); sigmoid(s), or sigmoid(s) + b
+// (sigmoid scoring).  k + 1 rounds of a row arg-max over (key, -index) (the
+// (k+1)-th best only for the near-tie flag); a winner's key is cleared, which
+// ranks it below every present key (present keys are at least 1).  The weights
+// are then built once from the chosen experts' scores, read back from the tile:
+//   softmax then top-k:  e = exp(s - max s), w = e / z (z: all experts), or
+//                        e / (sum of the chosen e) with renorm
+//   top-k then softmax:  softmax over the chosen s
+//   sigmoid then top-k:  g / (sum of the chosen g), g = sigmoid(s)
+// exp is the hardware exponential (v_exp_f32, about 1 ulp) and the divisions use
+// the hardware reciprocal: the weights are compared to 1e-4 relative.
+template <int NB, int SPL, int PASSES, bool WRITE_SCORES, int NW = 4>
 __device__ void select_tile(const float* tile, int stride, int t0, int T, int E, int k, int mode, int renorm,
                             const float* __restrict__ sel_bias, float* __restrict__ logits,
                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -117,9 +116,16 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
     const int e = r + 16 * i;
     sb[i] = biased ? sel_bias[min(e, E - 1)] : 0.f;
   }
+  // the score output: rows t0 .. t0 + 16 PASSES - 1 that exist; a buffer store
+  // past the range (dead rows, experts >= E) is dropped, so no store sits under
+  // a branch
+  const int live_rows = max(0, min(4 * NW * PASSES, T - t0));
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(WRITE_SCORES ? logits + (size_t)t0 * E : logits), (short)0,
+      WRITE_SCORES ? (int)((uint32_t)live_rows * (uint32_t)E * 4u) : 0, kBufferFlags);
 #pragma unroll 1
   for (int pass = 0; pass < PASSES; ++pass) {
-    const int lr = pass * 16 + wave * 4 + row;
+    const int lr = pass * 4 * NW + wave * 4 + row;
     const int t = t0 + lr;
     const bool live = t < T;
     const float* s = tile + lr * stride;
@@ -128,100 +134,94 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
     for (int i = 0; i < NB; ++i) {
       const int e = r + 16 * i;
       const bool present = e < E;
-      const float v = (present && live) ? s[e] : 0.f;
-      kf[i] = v;
-      if (WRITE_SCORES && present && live) logits[(size_t)t * E + e] = v;
+      kf[i] = (present && live) ? s[e] : 0.f;
+      if (WRITE_SCORES)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kf[i]), rl,
+                                              present ? (int)(((uint32_t)lr * (uint32_t)E + e) * 4u) : (int)0x80000000,
+                                              0, 0);
     }
-    // softmax maximum and denominator over all E
-    float m = 0.f, z = 0.f;
-    float ev[NB];
+    // softmax maximum and denominator over all E (softmax scoring)
+    float m = -INFINITY, z = 0.f;
     if (mode == MOE_SOFTMAX_THEN_TOPK) {
-      m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < NB; ++i)
         if (r + 16 * i < E) m = fmaxf(m, kf[i]);
       m = row16_max(m);
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        ev[i] = r + 16 * i < E ? expf(kf[i] - m) : 0.f;
-        z += ev[i];
-      }
+      for (int i = 0; i < NB; ++i) z += r + 16 * i < E ? __expf(kf[i] - m) : 0.f;
       z = row16_sum(z);
     }
-    float bv[NB];
-    uint32_t ko[NB];
+    const float rz = __builtin_amdgcn_rcpf(z);
+    uint64_t cand[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      float base, key;
-      if (mode == MOE_SOFTMAX_THEN_TOPK) {
-        base = ev[i];
-        key = biased ? ev[i] / z + sb[i] : kf[i];
-      } else if (mode == MOE_TOPK_THEN_SOFTMAX) {
-        base = kf[i];
-        key = biased ? kf[i] + sb[i] : kf[i];
-      } else {
-        base = 1.f / (1.f + expf(-kf[i]));
-        key = biased ? base + sb[i] : base;
+      float key;
+      if (mode == MOE_SOFTMAX_THEN_TOPK) key = biased ? __expf(kf[i] - m) * rz + sb[i] : kf[i];
+      else if (mode == MOE_TOPK_THEN_SOFTMAX) key = biased ? kf[i] + sb[i] : kf[i];
+      else {
+        const float g = __builtin_amdgcn_rcpf(1.f + __expf(-kf[i]));
+        key = biased ? g + sb[i] : g;
       }
-      bv[i] = base;
-      ko[i] = r + 16 * i < E ? max(order_key(key), 1u) : 0u;  // 0 marks "absent or taken"
+      const uint32_t ko = r + 16 * i < E ? max(order_key(key), 1u) : 0u;  // 0: absent or taken
+      cand[i] = ((uint64_t)ko << 32) | (uint32_t)~(uint32_t)(r + 16 * i);
     }
     const int rounds = k < E ? k + 1 : k;
     uint32_t my_idx[SPL];
-    float my_val[SPL];
 #pragma unroll
-    for (int q = 0; q < SPL; ++q) { my_idx[q] = 0u; my_val[q] = 0.f; }
-    float kth = 0.f, next = 0.f, vsum = 0.f, vmax = 0.f;
+    for (int q = 0; q < SPL; ++q) my_idx[q] = 0u;
+    uint32_t kth = 0u, next = 0u;
     for (int j = 0; j < rounds; ++j) {
-      uint32_t bo = 0u, bi = 0xffffffffu;
-      float bval = 0.f;
+      uint64_t best = cand[0];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        if (ko[i] > bo) { bo = ko[i]; bi = r + 16 * i; bval = bv[i]; }  // strict: the lower index keeps a tie
-      argmax_step<kDppXor1>(bo, bi, bval);
-      argmax_step<kDppXor2>(bo, bi, bval);
-      argmax_step<kDppHalfMirror>(bo, bi, bval);
-      argmax_step<kDppMirror>(bo, bi, bval);
-      const float wkey = key_value(bo);
+      for (int i = 1; i < NB; ++i) best = cand[i] > best ? cand[i] : best;
+      pmax_step<kDppXor1>(best);
+      pmax_step<kDppXor2>(best);
+      pmax_step<kDppHalfMirror>(best);
+      pmax_step<kDppMirror>(best);
+      const uint32_t widx = ~(uint32_t)best, wkey = (uint32_t)(best >> 32);
       if (j < k) {
         if (j == k - 1) kth = wkey;
-        if (mode == MOE_TOPK_THEN_SOFTMAX) {  // running softmax over the chosen scores
-          if (j == 0) {
-            vmax = bval;
-            vsum = 1.f;
-          } else if (bval > vmax) {
-            vsum = vsum * expf(vmax - bval) + 1.f;
-            vmax = bval;
-          } else {
-            vsum += expf(bval - vmax);
-          }
-        } else {
-          vsum += bval;
-        }
 #pragma unroll
         for (int q = 0; q < SPL; ++q)
-          if (j == r + 16 * q) { my_idx[q] = bi; my_val[q] = bval; }
+          if (j == r + 16 * q) my_idx[q] = widx;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-          if (bi == (uint32_t)(r + 16 * i)) ko[i] = 0u;
+          if (widx == (uint32_t)(r + 16 * i)) cand[i] &= 0xffffffffull;  // taken
       } else {
         next = wkey;
       }
     }
+    // weights from the chosen scores; slot j = r + 16 q
+    float sv[SPL], part = 0.f, vmax = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+      const bool slot = r + 16 * q < k;
+      sv[q] = slot && live ? s[my_idx[q]] : 0.f;
+      if (slot) vmax = fmaxf(vmax, sv[q]);
+    }
+    if (mode == MOE_TOPK_THEN_SOFTMAX) vmax = row16_max(vmax);
+    float base[SPL];
+#pragma unroll
+    for (int q = 0; q < SPL; ++q) {
+      const bool slot = r + 16 * q < k;
+      if (mode == MOE_SOFTMAX_THEN_TOPK) base[q] = __expf(sv[q] - m);
+      else if (mode == MOE_TOPK_THEN_SOFTMAX) base[q] = __expf(sv[q] - vmax);
+      else base[q] = __builtin_amdgcn_rcpf(1.f + __expf(-sv[q]));
+      part += slot ? base[q] : 0.f;
+    }
+    const bool own_sum = mode != MOE_SOFTMAX_THEN_TOPK || renorm;
+    const float rden = __builtin_amdgcn_rcpf(own_sum ? row16_sum(part) : z);
     if (live) {
 #pragma unroll
       for (int q = 0; q < SPL; ++q) {
         const int j = r + 16 * q;
         if (j < k) {
-          float w;
-          if (mode == MOE_SOFTMAX_THEN_TOPK) w = my_val[q] / (renorm ? vsum : z);
-          else if (mode == MOE_TOPK_THEN_SOFTMAX) w = expf(my_val[q] - vmax) / vsum;
-          else w = my_val[q] / vsum;
           topk_idx[(size_t)t * k + j] = (int32_t)my_idx[q];
-          topk_w[(size_t)t * k + j] = w;
+          topk_w[(size_t)t * k + j] = base[q] * rden;
         }
       }
-      if (r == 0) near_tie[t] = (k < E && ((double)kth - (double)next) < MOE_NEAR_TIE_GAP) ? 1 : 0;
+      if (r == 0)
+        near_tie[t] = (k < E && ((double)key_value(kth) - (double)key_value(next)) < MOE_NEAR_TIE_GAP) ? 1 : 0;
     }
   }
 }
@@ -387,42 +387,47 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 }
 
 // Scores as a GEMM with DMA-fed LDS stages, then selection, for many tokens and
-// 64 < E <= 128.  Block: 32 tokens and every expert; two blocks per CU, so that
-// one block's selection (serial DPP rounds) overlaps the other's loads.  Wave w
-// multiplies experts 32 w .. 32 w + 31 against the 32 tokens (32x32x16 MFMA,
-// router rows as the "A" operand), so an x byte is read from HBM once.
-//  * Each K step of 64 loads the block's 32 x rows and E router rows (128 bytes
+// 64 < E <= 128.  Block: 8 NW tokens and every expert on NW waves (NW = 4 or 8):
+// wave w multiplies experts 32 (w % 4) .. 32 (w % 4) + 31 against tokens
+// 32 (w / 4) .. 32 (w / 4) + 31 (32x32x16 MFMA, router rows as the "A" operand),
+// so an x byte is read from HBM once and a router row once per block.  The
+// selection then runs on the same waves.
+//  * NW = 8 (64 tokens, one block per CU) halves the router reads from L2, which
+//    bound the loop once every CU is busy; NW = 4 (32 tokens, two blocks per CU)
+//    keeps more CUs busy when T is small.
+//  * Each K step of 64 loads the block's x rows and E router rows (128 bytes
 //    each: whole lines) straight into LDS (buffer_load_dwordx4 ... lds writes
 //    lane l's 16 bytes at M0 + 16 l), three stages deep; each stage is its own
 //    __shared__ array, so the compiler waits only for the DMA a read needs.
 //    16-byte chunk c of LDS row r sits at position c ^ ((r & 7) ^ ((r >> 3) & 1)):
 //    conflict-free fragment reads.
-//  * The score tile then takes stage 0's memory.
-//  * Measured (qwen3 shape, router alone, x in cache): T = 16384 28.4 us against
-//    35.9 for the register-operand scores and the separate selection; T = 2304
-//    17.7 vs 20.7.  64 tokens a block (one per CU) ran 32-33 us: its four
-//    selection passes did not overlap anything.  A six-deep x ring beside a
-//    three-deep router ring ran slower (31.4 us).
-constexpr int kGemmTokens = 32;
+//  * Measured (qwen3 shape, router alone, x in cache): T = 16384 24.3 us with 64
+//    tokens, 26.8 with 32, 35.9 for the register-operand scores and the separate
+//    selection; T = 4096 18.9 / 20.2; T = 2304 18.4 / 16.8 (36 against 72 busy CUs).
+//    A six-deep x ring beside a three-deep router ring ran slower (31.4 us).
 constexpr int kGemmStages = 3;
+constexpr int kGemmWideMinT = 4096;  // 64-token blocks from this T on
 __device__ __forceinline__ int route_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 typedef __attribute__((address_space(3))) void* route_lds_t;
 
-template <int SPL>
-__global__ __launch_bounds__(256, 2) void route_gemm_kernel(
+template <int SPL, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ near_tie) {
-  constexpr int EP = 128, BK = 64, TT = kGemmTokens;
-  constexpr int STAGE = (TT + EP) * BK;  // bf16: 32 x rows, then 128 router rows (20 KB)
+  static_assert(NW == 4 || NW == 8, "32 or 64 tokens a block");
+  constexpr int EP = 128, BK = 64, TT = 8 * NW;
+  constexpr int RPW = 16 / NW;           // router DMA instructions per wave and step
+  constexpr int STAGE = (TT + EP) * BK;  // bf16: TT x rows, then 128 router rows
   constexpr int TSTR = EP + 4;           // score tile stride (floats)
-  static_assert(TT * TSTR * 4 <= STAGE * 2, "the score tile fits in a stage");
   __shared__ __attribute__((aligned(1024))) uint16_t s0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s2[STAGE];
+  __shared__ __attribute__((aligned(16))) float tile[TT * TSTR];
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int eg = wave & 3, th = wave >> 2;
   const int t0 = blockIdx.x * TT;
   const int rows = min(TT, T - t0);
   const int nst = d / BK;
@@ -434,17 +439,17 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(
       (void*)wr, (short)0, (int)((uint32_t)E * (uint32_t)d * 2u), kBufferFlags);
   constexpr uint32_t kOut = 0x80000000u;  // past every resource: reads zeros
 
-  // DMA: a step is 4 x instructions (8 rows each) and 16 router instructions;
-  // wave w issues x instruction w and router instructions 4w .. 4w + 3.  Lane l:
-  // row 8 j + l / 8 of instruction j, position l % 8, global chunk
+  // DMA: a step is NW x instructions (8 rows each) and 16 router instructions;
+  // wave w issues x instruction w and router instructions RPW w .. RPW w + RPW - 1.
+  // Lane l: row 8 j + l / 8 of instruction j, position l % 8, global chunk
   // (l % 8) ^ (l / 8) ^ (j & 1).
   const int c0 = (lane & 7) ^ (lane >> 3);
   const uint32_t xo =
       ((uint32_t)min(8 * wave + (lane >> 3), rows - 1) * (uint32_t)d + 8u * (c0 ^ (wave & 1))) * 2u;
-  uint32_t wo[4];
+  uint32_t wo[RPW];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int j = 4 * wave + u;
+  for (int u = 0; u < RPW; ++u) {
+    const int j = RPW * wave + u;
     const int n = 8 * j + (lane >> 3);
     wo[u] = n < E ? ((uint32_t)n * (uint32_t)d + 8u * (c0 ^ (j & 1))) * 2u : kOut;
   }
@@ -452,11 +457,15 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(
   auto dma = [&](uint16_t* st, int s) __attribute__((always_inline)) {
     const int kb = 2 * BK * min(s, nst - 1);
     const uint32_t pad = s < nst ? 0u : kOut;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (route_lds_t)(st + 8 * wave * BK), 16, xo | pad, kb, 0, 0);
+    const route_lds_t xdst = (route_lds_t)(st + 8 * wave * BK);
+    const uint32_t xoff = xo | pad;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, xdst, 16, xoff, kb, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (route_lds_t)(st + (TT + 8 * (4 * wave + u)) * BK), 16,
-                                               wo[u] | pad, kb, 0, 0);
+    for (int u = 0; u < RPW; ++u) {
+      const route_lds_t wdst = (route_lds_t)(st + (TT + 8 * (RPW * wave + u)) * BK);
+      const uint32_t woff = wo[u] | pad;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, wdst, 16, woff, kb, 0, 0);
+    }
   };
   // Fragments: lane l reads row l % 32 of a 32-row block, chunk 2 ks + l / 32.
   const int frow = lane & 31, fsw = route_swz(frow);
@@ -466,8 +475,8 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int pos = 8 * ((2 * ks + (lane >> 5)) ^ fsw);
-      wf[ks] = as_bf16x8(ld16(st + (TT + 32 * wave + frow) * BK + pos));
-      xf[ks] = as_bf16x8(ld16(st + frow * BK + pos));
+      wf[ks] = as_bf16x8(ld16(st + (TT + 32 * eg + frow) * BK + pos));
+      xf[ks] = as_bf16x8(ld16(st + (32 * th + frow) * BK + pos));
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) acc = mfma32x32x16(wf[ks], xf[ks], acc);
@@ -488,22 +497,19 @@ __global__ __launch_bounds__(256, 2) void route_gemm_kernel(
     step(s1, s0, s + 1);
     step(s2, s1, s + 2);
   }
-  // the padding DMAs (zeros, past the last step) land, and every wave is done
-  // with the stages, before stage 0 takes the score tile
+  // the padding DMAs (zeros, past the last step) land before the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  float* tile = reinterpret_cast<float*>(s0);
-  // accumulator element e of lane l: expert 32 w + 8 (e / 4) + 4 (l / 32) + e % 4,
-  // token l % 32
+  // accumulator element e of lane l: expert 32 eg + 8 (e / 4) + 4 (l / 32) + e % 4,
+  // token 32 th + l % 32
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int n = 32 * wave + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
+    const int n = 32 * eg + 8 * (e / 4) + 4 * (lane >> 5) + (e & 3);
     const float b = (bias != nullptr && n < E) ? bias[n] : 0.f;
-    tile[frow * TSTR + n] = acc[e] + b;
+    tile[(32 * th + frow) * TSTR + n] = acc[e] + b;
   }
   __syncthreads();
-  select_tile<8, SPL, TT / 16, true>(tile, TSTR, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx, topk_w,
-                                      near_tie);
+  select_tile<8, SPL, TT / (4 * NW), true, NW>(tile, TSTR, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx,
+                                                topk_w, near_tie);
 }
 
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
@@ -614,10 +620,14 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
                        a.near_tie);
   } else if (a.dtype == MOE_BF16 && NB == 8 && MOE_ROUTE_GEMM) {
     // 64 < E <= 128: scores as a DMA-fed GEMM, selection in the same block
-    hipLaunchKernelGGL((route_gemm_kernel<SPL>), dim3((a.T + kGemmTokens - 1) / kGemmTokens), block, 0, stream,
-                       (const uint16_t*)a.x,
-                       (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E, a.k, a.mode, a.renorm,
-                       a.logits, a.topk_idx, a.topk_w, a.near_tie);
+    if (a.T >= kGemmWideMinT)
+      hipLaunchKernelGGL((route_gemm_kernel<SPL, 8>), dim3((a.T + 63) / 64), dim3(512), 0, stream,
+                         (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
+                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
+    else
+      hipLaunchKernelGGL((route_gemm_kernel<SPL, 4>), dim3((a.T + 31) / 32), dim3(256), 0, stream,
+                         (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
+                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
   } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
              (int64_t)a.T * ((a.E + kScoreSplitExperts - 1) / kScoreSplitExperts) <= kScoreSplitMaxRowReads) {
     // many experts: 64-expert score blocks (two per CU), then selection; each block
