@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--configs", action="store_true",
                    help="instead of the headline line, time the whole layer on every configured shape "
                         "(one JSON line per shape; generating the largest weight set takes a while)")
+    p.add_argument("--combine-compare", default="", metavar="W1,W2,...",
+                   help="time the gather and the scatter combine on these workloads")
     p.add_argument("--sweep-tokens", default="", metavar="T1,T2,...",
                    help="instead of the headline line, time the --workload layer at each token count "
                         "(same weights; one JSON line each)")
@@ -119,8 +121,8 @@ def measured_copy_rate(torch, nbytes: int = 1 << 30) -> float:
 
 
 def timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=0.0):
-    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up, down and
-    the shared expert (0 without one)).
+    """Run warmup + timed steps; returns (ms per step, per-launch ms of gate/up, down (with
+    the scatter combine: down and combine) and the shared expert (0 without one)).
     With large groups the balance statistics run on a second stream beside the
     combine (MoeLayer.forward); a step ends when both streams are done.  The timed
     steps record no events inside; the per-launch GEMM times come from as many
@@ -169,6 +171,8 @@ def timed_steps(layer, x, bufs, steps, warmup, stream, torch, min_warm_ms=0.0):
     gu = [e[0].elapsed_time(e[1]) for e in evs]
     dn = [e[1].elapsed_time(e[2]) for e in evs]
     sh = [e[2].elapsed_time(e[3]) for e in evs]
+    if getattr(layer, "scatter_combine", False):
+        dn, sh = sh, dn  # the shared expert runs before the down GEMM with the combine
     return total / steps, float(np.mean(gu)), float(np.mean(dn)), float(np.mean(sh))
 
 
@@ -320,6 +324,49 @@ def config_sweep(steps: int, warmup: int):
         torch.cuda.empty_cache()
 
 
+def combine_compare(names, steps: int, warmup: int, rounds: int = 3):
+    """The layer with the gather combine (the down GEMM writes y_perm, a second
+    kernel sums each token's rows in slot order) against the scatter combine (the
+    down GEMM adds its weighted rows into a float32 accumulator with atomics, then
+    one pass adds the shared expert and rounds).  Same weights and inputs; the two
+    forms are timed in alternation, `rounds` times each, and the median kept.  One
+    JSON line per workload: whole-step times, and the down launch alone (gather)
+    against the down-with-combine call (scatter)."""
+    import torch
+
+    from mixture_experts_ffn_08_amd import inputs as minp
+    from mixture_experts_ffn_08_amd.layer import Buffers, DeviceWeights, MoeLayer, to_device
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    for name in names:
+        shape = minp.SHAPES[name]
+        inp = minp.LayerInputs(shape, seed=0)
+        weights = DeviceWeights(inp, "cuda:0")
+        x = to_device(inp.x, shape.dtype, "cuda:0")
+        forms = {"gather": MoeLayer(weights), "scatter": MoeLayer(weights, scatter_combine=True)}
+        bufs = {k: Buffers(shape, shape.T, "cuda:0", scatter=(k == "scatter")) for k in forms}
+        res = {k: [] for k in forms}
+        with torch.cuda.stream(stream):
+            for r in range(rounds):
+                for k, lay in forms.items():
+                    ms, gu, dn, sh = timed_steps(lay, x, bufs[k], steps, warmup, stream, torch, min_warm_ms=150.0)
+                    res[k].append((ms, gu, dn, sh))
+        med = {k: np.median(np.array(v), axis=0) for k, v in res.items()}
+        y_diff = float((bufs["gather"].y.float() - bufs["scatter"].y.float()).abs().max().item())
+        print(json.dumps({
+            "workload": name, "T": shape.T, "d": shape.d, "E": shape.E, "k": shape.k,
+            "gather_ms_per_step": float(med["gather"][0]), "scatter_ms_per_step": float(med["scatter"][0]),
+            "scatter_speedup": float(med["gather"][0] / med["scatter"][0]),
+            "gather_down_ms": float(med["gather"][2]),
+            "scatter_down_combine_ms": float(med["scatter"][2]),
+            "gather_steps_ms_all": [round(v[0], 4) for v in res["gather"]],
+            "scatter_steps_ms_all": [round(v[0], 4) for v in res["scatter"]],
+            "max_abs_y_diff": y_diff, "steps": steps, "warmup": warmup, "rounds": rounds}), flush=True)
+        del weights, x, forms, bufs, inp
+        torch.cuda.empty_cache()
+
+
 def token_sweep(name: str, tokens, steps: int, warmup: int):
     """The layer of workload `name` at other token counts, on one set of weights:
     ms per step, the two GEMM launches, and the touched experts' weight bytes
@@ -362,6 +409,9 @@ def main():
         return
     if args.configs:
         config_sweep(args.steps, args.warmup)
+        return
+    if args.combine_compare:
+        combine_compare(args.combine_compare.split(","), args.steps, args.warmup)
         return
     if args.sweep_tokens:
         token_sweep(args.workload, [int(v) for v in args.sweep_tokens.split(",")], args.steps, args.warmup)

@@ -297,6 +297,39 @@ int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const flo
                 hipStream_t stream);
 
 /*
+ * moe_grouped_down_combine -- moe_grouped_down and moe_combine in one call, with
+ * the weighted sum done in the down GEMM's epilogue: each product row r, rounded
+ * to dtype as y_perm would hold it, is multiplied by its slot's gate weight and
+ * added with float32 atomics to an accumulator row of token perm_token[r]; y is
+ * then accumulator + shared_y, rounded once.  No y_perm is written or read.
+ * Sources: ML Interview Notes, MoELayer (out[tok] += weights * expert(x), a
+ * weighted scatter-add); The Residual Stream, "An MoE tiny GPT" (index_add_ of
+ * the weighted expert outputs); Transformers & Math 17.2 equation (plus the
+ * shared expert, unweighted).
+ * The result equals moe_grouped_down followed by moe_combine up to the order of
+ * the float32 additions, which atomics do not fix: y may differ from run to run
+ * in the last bit of a sum before rounding (at most one dtype ulp after it).
+ *
+ *   a, offsets, G, max_rows, F, d, w_down, dtype   as for moe_grouped_down
+ *   perm_token device [max_rows] int32: the token of each row (moe_permute's
+ *            perm_token, or moe_permute_padded's slot_token, -1 for padding);
+ *            rows whose value lies outside [0, T) add nothing.  It must be the
+ *            inverse of row_of, as those calls write it.
+ *   row_of, topk_w, shared_y, T, k, y              as for moe_combine (y_rows =
+ *            max_rows: row_of values outside [0, max_rows) count as dropped)
+ *   workspace device, >= moe_down_combine_workspace_bytes(T, d, max_rows) bytes:
+ *            the float32 accumulator [T][d] and one weight per row; zeroed and
+ *            written by the call itself
+ * Calls on one stream are ordered; two calls that share a workspace must not
+ * run concurrently.
+ */
+int moe_grouped_down_combine(const void* a, const int32_t* offsets, int G, int max_rows, int F, int d,
+                             const void* w_down, int dtype, const int32_t* perm_token, const int32_t* row_of,
+                             const float* topk_w, int T, int k, const void* shared_y, void* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+size_t moe_down_combine_workspace_bytes(int T, int d, int max_rows);
+
+/*
  * moe_stats -- balance statistics.
  * Sources: Transformers & Math 17.4 equation (L_aux = alpha N_E sum f_i P_i);
  * The Residual Stream "Keeping the load even" and the MoE listing (f = counts /

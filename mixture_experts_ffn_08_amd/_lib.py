@@ -24,7 +24,7 @@ MOE_MAX_EXPERTS = 256
 EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_noalloc", "moe_permute_padded",
            "moe_permute_workspace_bytes", "moe_capacity",
            "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
-           "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
+           "moe_grouped_down_combine", "moe_down_combine_workspace_bytes", "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -42,6 +42,8 @@ _SIGS = {
     "moe_grouped_down": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P]),
     "moe_grouped_swiglu": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P]),
     "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_grouped_down_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
+    "moe_down_combine_workspace_bytes": (_SZ, [_I, _I, _I]),
     "moe_stats": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_stats_workspace_bytes": (_SZ, [_I, _I]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
@@ -243,6 +245,26 @@ def moe_combine(y_perm, row_of, topk_w, shared_y, T, k, d, y, stream=None, y_row
             _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), dt, T, k, d,
             _dev(y, "y", y.dtype, T * d), _stream(stream))
     _check("moe_combine", load().moe_combine(*args))
+
+
+def moe_down_combine_workspace_bytes(T, d, max_rows) -> int:
+    return int(load().moe_down_combine_workspace_bytes(T, d, max_rows))
+
+
+def moe_grouped_down_combine(a, offsets, G, max_rows, F, d, w_down, perm_token, row_of, topk_w, T, k, shared_y, y,
+                             workspace, stream=None):
+    """The down GEMM with the combine in its epilogue (fp32 atomics into the
+    workspace), then y = that sum + shared_y, rounded once."""
+    dt = _dtype_code(y)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    args = (_dev(a, "a", y.dtype, max_rows * F, optional=max_rows == 0),
+            _dev(offsets, "offsets", torch.int32, G + 1, optional=max_rows == 0), G, max_rows, F, d,
+            _dev(w_down, "w_down", y.dtype, G * d * F, optional=max_rows == 0), dt,
+            _dev(perm_token, "perm_token", torch.int32, max_rows, optional=max_rows == 0),
+            _dev(row_of, "row_of", torch.int32, T * k), _dev(topk_w, "topk_w", torch.float32, T * k), T, k,
+            _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), _dev(y, "y", y.dtype, T * d),
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check("moe_grouped_down_combine", load().moe_grouped_down_combine(*args))
 
 
 def moe_stats(counts, logits, T, k, E, alpha, f, P, l_aux, max_over_mean, workspace, stream=None):

@@ -390,6 +390,52 @@ int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const flo
   return hip_status(moe::launch_combine(c, stream), fn);
 }
 
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t moe_down_combine_workspace_bytes(int T, int d, int max_rows) {
+  if (T < 0 || d < 0 || max_rows < 0) return 0;
+  return round256((size_t)T * (size_t)d * 4u) + round256((size_t)max_rows * 4u);
+}
+
+int moe_grouped_down_combine(const void* a, const int32_t* offsets, int G, int max_rows, int F, int d,
+                             const void* w_down, int dtype, const int32_t* perm_token, const int32_t* row_of,
+                             const float* topk_w, int T, int k, const void* shared_y, void* y, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  static const char* fn = "moe_grouped_down_combine";
+  CHECK(grouped_check(fn, G, max_rows, d, F, dtype));
+  if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (k < 1) return fail(MOE_ERR_INVALID_ARG, "%s: k = %d < 1", fn, k);
+  CHECK(assignments_check(fn, T, k));
+  if (T == 0) return ok();
+  NEED(row_of, fn);
+  NEED(topk_w, fn);
+  NEED(y, fn);
+  if (max_rows > 0) {
+    NEED(a, fn);
+    NEED(offsets, fn);
+    NEED(w_down, fn);
+    NEED(perm_token, fn);
+  }
+  const size_t need = moe_down_combine_workspace_bytes(T, d, max_rows);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  float* y_acc = static_cast<float*>(workspace);
+  float* row_w = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256((size_t)T * (size_t)d * 4u));
+  hipError_t e = moe::launch_scatter_prologue(y_acc, row_w, row_of, topk_w, T, k, d, max_rows, stream);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (max_rows > 0) {
+    moe::GroupedGemmArgs g{a, nullptr, max_rows, offsets, G, max_rows, d, F, w_down, nullptr, nullptr, dtype};
+    g.out_tok = perm_token;
+    g.out_w = row_w;
+    g.y_acc = y_acc;
+    g.T = T;
+    e = moe::launch_grouped_gemm(g, false, stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return hip_status(moe::launch_scatter_finish(y_acc, shared_y, dtype, T, d, y, stream), fn);
+}
+
 int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, float alpha, float* f, float* P,
               float* l_aux, float* max_over_mean, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {

@@ -160,10 +160,97 @@ hipError_t launch_dtype(const CombineArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Scatter combine (the weighted sum done by the down GEMM's epilogue, as the
+// weighted scatter-add of ML Interview Notes, MoELayer and The Residual Stream,
+// "An MoE tiny GPT"): before the GEMM, zero the fp32 accumulator and give each
+// kept row its slot's gate weight; after it, add the shared expert and round once.
+__global__ __launch_bounds__(256) void scatter_prologue_kernel(float* __restrict__ y_acc, float* __restrict__ row_w,
+                                                                const int32_t* __restrict__ row_of,
+                                                                const float* __restrict__ topk_w, int64_t n4,
+                                                                int64_t pairs, int max_rows) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n4) reinterpret_cast<float4*>(y_acc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (i < pairs) {
+    const int r = row_of[i];
+    if (r >= 0 && r < max_rows) row_w[r] = topk_w[i];
+  }
+}
+
+// One 16-byte output chunk per thread: y = y_acc + shared_y, one rounding.
+template <bool BF16, bool SHARED>
+__global__ __launch_bounds__(256) void scatter_finish_kernel(const float* __restrict__ y_acc,
+                                                              const void* __restrict__ shared_y, int64_t chunks,
+                                                              void* __restrict__ y) {
+  constexpr int EPC = BF16 ? 8 : 4;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  float acc[EPC];
+  const u32x4 a0 = ld16_nt(y_acc + c * EPC);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = __uint_as_float(a0[q]);
+  if (BF16) {
+    const u32x4 a1 = ld16_nt(y_acc + c * EPC + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[4 + q] = __uint_as_float(a1[q]);
+  }
+  if (SHARED) {
+    const u32x4 v = ld16_nt(static_cast<const char*>(shared_y) + c * 16);
+    if (BF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(v[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(v[q] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
+    }
+  }
+  u32x4 o;
+  if (BF16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+  }
+  st16_nt(static_cast<char*>(y) + c * 16, o);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   return a.dtype == MOE_BF16 ? launch_dtype<true>(a, stream) : launch_dtype<false>(a, stream);
+}
+
+hipError_t launch_scatter_prologue(float* y_acc, float* row_w, const int32_t* row_of, const float* topk_w, int T,
+                                   int k, int d, int max_rows, hipStream_t stream) {
+  const int64_t n4 = (int64_t)T * d / 4, pairs = (int64_t)T * k;
+  const int64_t n = n4 > pairs ? n4 : pairs;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_prologue_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, y_acc, row_w,
+                     row_of, topk_w, n4, pairs, max_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_finish(const float* y_acc, const void* shared_y, int dtype, int T, int d, void* y,
+                                 hipStream_t stream) {
+  const bool bf16 = dtype == MOE_BF16;
+  const int64_t chunks = (int64_t)T * d / (bf16 ? 8 : 4);
+  if (chunks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((chunks + 255) / 256)), block(256);
+  if (bf16) {
+    if (shared_y != nullptr)
+      hipLaunchKernelGGL((scatter_finish_kernel<true, true>), grid, block, 0, stream, y_acc, shared_y, chunks, y);
+    else
+      hipLaunchKernelGGL((scatter_finish_kernel<true, false>), grid, block, 0, stream, y_acc, nullptr, chunks, y);
+  } else {
+    if (shared_y != nullptr)
+      hipLaunchKernelGGL((scatter_finish_kernel<false, true>), grid, block, 0, stream, y_acc, shared_y, chunks, y);
+    else
+      hipLaunchKernelGGL((scatter_finish_kernel<false, false>), grid, block, 0, stream, y_acc, nullptr, chunks, y);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -64,6 +64,11 @@
 namespace moe {
 namespace {
 
+// y += v at device scope, result unused: one global_atomic_add_f32 (no return).
+__device__ __forceinline__ void atomic_add_f32(float* y, float v) {
+  __hip_atomic_fetch_add(y, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 constexpr int BN = 256, BK = 64;
 constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row (16-byte pad)
 // Block tile rows by the average rows per group: 128 up to kSmallTileRowsPerGroup,
@@ -162,11 +167,13 @@ __device__ void locate(int G, const TileScan& s, int n_tiles, int t, int& g, int
 }
 
 
-template <bool DUAL, int BM, bool EARLY>
+template <bool DUAL, int BM, bool EARLY, bool SCATTER>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int n_tiles) {
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int n_tiles, const int32_t* __restrict__ out_tok,
+    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out) {
+  static_assert(!(SCATTER && DUAL), "the scatter form is single");
   constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
   constexpr int NAC = BM / 32;                   // A chunks per thread per K step
   // Wave layout.  BM = 256: the 4 waves as 2 x 2, each 128 rows x 128 B rows (dual:
@@ -535,6 +542,40 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
           }
       }
     };
+    // Scatter form: wave w takes LDS rows w, w + 4, ... of a pass; lane l < RPW
+    // fetches the token and weight of the wave's row l, which every lane then
+    // reads as scalars.  A row's columns go out as fp32 atomic adds with lane l
+    // on columns l + 64 c, so that one instruction covers 256 contiguous bytes.
+    auto scatter_out = [&](auto pass) {
+      constexpr int P = decltype(pass)::value;
+      constexpr int RPW = PROWS / 4;  // rows per wave and pass
+      static_assert(RPW <= 64, "a row per lane");
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      const int lr_l = wv + 4 * min(lane, RPW - 1);
+      const int trow_l = BM == 256 && PASSES == 2 ? (lr_l >= 64 ? 128 : 0) + 64 * P + (lr_l & 63) : lr_l + P * PROWS;
+      int tok_l = -1;
+      float w_l = 0.f;
+      if (lane < RPW && trow_l < e_rows) {
+        tok_l = out_tok[e_row0 + trow_l];
+        w_l = out_w[e_row0 + trow_l];
+      }
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int tok = __builtin_amdgcn_readlane(tok_l, i);
+        if (tok < 0 || tok >= T_out) continue;  // past the group, padding, or not a token
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_l), i));
+        const uint16_t* orow = ot + (wv + 4 * i) * OST;
+        float* yr = y_acc + (size_t)tok * N + e_n0;
+#pragma unroll
+        for (int c = 0; c < TN / 64; ++c) {
+          const int col = lane + 64 * c;
+          if (col < ncols) atomic_add_f32(yr + col, w * bf16_to_f32(orow[col]));
+        }
+      }
+    };
+    auto emit = [&](auto pass) {
+      if constexpr (SCATTER) scatter_out(pass); else store_out(pass);
+    };
     using P0 = std::integral_constant<int, 0>;
     using P1 = std::integral_constant<int, 1>;
     // The next tile's step 0 goes to stage 0 and its step 2 is loaded ahead of
@@ -549,12 +590,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     if constexpr (EARLY && PASSES == 2) store(R0{}, 0);
     lds_barrier();
     if constexpr (EARLY && PASSES == 2) load(R0{}, 2 * BK);
-    store_out(P0{});
+    emit(P0{});
     if constexpr (PASSES == 2) {
       lds_barrier();  // every wave has read the first pass
       write_out(P1{});
       lds_barrier();
-      store_out(P1{});
+      emit(P1{});
     }
     if (!more) break;
     tile = next;
@@ -577,11 +618,13 @@ __host__ __device__ constexpr int sk_bn(bool dual) { return dual ? 64 : 128; }
 constexpr int SK_CHUNK = 128; // K per chunk
 constexpr int kSkinnyTwoTilesAbove = 10;  // rows per group (average) above which a pass takes two token tiles
 
-template <bool DUAL, bool GATHER, int TT>
+template <bool DUAL, bool GATHER, int TT, bool SCATTER = false>
 __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const int32_t* __restrict__ out_tok = nullptr,
+    const float* __restrict__ out_w = nullptr, float* __restrict__ y_acc = nullptr, int T_out = 0) {
+  static_assert(!(SCATTER && DUAL), "the scatter form is single");
   const int nblk_n = N / sk_bn(DUAL);
   // each XCD streams one contiguous eighth of the weights
   const int lb = xcd_contiguous_block();
@@ -696,6 +739,21 @@ __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
             v[i] = silu_bf16out(x) * acc[tt][1][i];
           }
           *reinterpret_cast<uint2*>(crow) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        } else if (SCATTER) {
+          // the product rounded to bf16, as C would hold it, times the row's weight
+          const int tok = out_tok[row];
+          if (tok >= 0 && tok < T_out) {
+            const float w = out_w[row];
+            float* yr = y_acc + (size_t)tok * N + n_base + 4 * q;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; i += 2) {
+                const uint32_t pk = pack_bf16x2(acc[tt][b][i], acc[tt][b][i + 1]);
+                atomic_add_f32(yr + b * SK_ROWS + i, w * __uint_as_float(pk << 16));
+                atomic_add_f32(yr + b * SK_ROWS + i + 1, w * __uint_as_float(pk & 0xffff0000u));
+              }
+          }
         } else {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
@@ -715,7 +773,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
                                                                 int max_rows, int N, int K,
                                                                 const float* __restrict__ B0,
                                                                 const float* __restrict__ B1,
-                                                                float* __restrict__ C) {
+                                                                float* __restrict__ C,
+                                                                const int32_t* __restrict__ out_tok,
+                                                                const float* __restrict__ out_w,
+                                                                float* __restrict__ y_acc, int T_out) {
   const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (id >= (int64_t)max_rows * N) return;
   const int row = (int)(id / N), n = (int)(id % N);
@@ -739,7 +800,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   } else {
     for (int i = 0; i < K; ++i) s0 = fmaf(a[i], b0[i], s0);
   }
-  C[(size_t)row * N + n] = s0;
+  if (y_acc != nullptr) {
+    const int tok = out_tok[row];
+    if (tok >= 0 && tok < T_out) atomic_add_f32(y_acc + (size_t)tok * N + n, out_w[row] * s0);
+  } else {
+    C[(size_t)row * N + n] = s0;
+  }
 }
 
 }  // namespace
@@ -760,6 +826,8 @@ int persistent_blocks() {
 }
 
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
+  const bool scatter = a.y_acc != nullptr;
+  if (scatter && (dual || a.a_rows != nullptr)) return hipErrorInvalidValue;
   if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
     // few rows per group on average: stream the weights, skip the 256-row tiles
     const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
@@ -767,7 +835,18 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
   hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA, TT>), grid, block, 0, stream, (const uint16_t*)a.A, \
                      a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,     \
                      D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C)
+#define MOE_SKINNY_SCATTER(TT)                                                                                \
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<false, false, TT, true>), grid, block, 0, stream,           \
+                     (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
+                     (const uint16_t*)a.B0, nullptr, nullptr, a.out_tok, a.out_w, a.y_acc, a.T)
     const bool gather = a.a_rows != nullptr;
+    if (scatter) {
+      // the scatter form runs on the down GEMM: single, no gather
+      if ((int64_t)a.max_rows > (int64_t)kSkinnyTwoTilesAbove * a.G) MOE_SKINNY_SCATTER(2);
+      else MOE_SKINNY_SCATTER(1);
+      return hipGetLastError();
+    }
+#undef MOE_SKINNY_SCATTER
     // two 16-row token tiles per weight pass once groups average over 10 rows (then
     // many groups exceed 16 rows, and one tile per pass would stream their weights twice)
     if ((int64_t)a.max_rows > (int64_t)kSkinnyTwoTilesAbove * a.G) {
@@ -796,16 +875,22 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
     const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
     // Step 2 of a tile can be loaded in the previous tile's epilogue when there is one (K >= 256).
     const bool early = a.K >= 4 * BK;
-#define MOE_TILED_E(D, M, E)                                                                                   \
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M, E>), dim3((unsigned)blocks), dim3(256), 0, stream,      \
+#define MOE_TILED_E(D, M, E, S)                                                                               \
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M, E, S>), dim3((unsigned)blocks), dim3(256), 0, stream,   \
                      (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
-                     (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles)
-#define MOE_TILED(D, M)          \
-  do {                           \
-    if (early)                   \
-      MOE_TILED_E(D, M, true);   \
-    else                         \
-      MOE_TILED_E(D, M, false);  \
+                     (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles,     \
+                     a.out_tok, a.out_w, a.y_acc, a.T)
+#define MOE_TILED(D, M)                                     \
+  do {                                                      \
+    if (early) {                                            \
+      if (D) MOE_TILED_E(D, M, true, false);                \
+      else if (scatter) MOE_TILED_E(false, M, true, true);  \
+      else MOE_TILED_E(false, M, true, false);              \
+    } else {                                                \
+      if (D) MOE_TILED_E(D, M, false, false);               \
+      else if (scatter) MOE_TILED_E(false, M, false, true); \
+      else MOE_TILED_E(false, M, false, false);             \
+    }                                                       \
   } while (0)
     if (bm == 128) {
       if (dual) MOE_TILED(true, 128); else MOE_TILED(false, 128);
@@ -822,11 +907,11 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
     if (dual)
       hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                          (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const float*)a.B0, (const float*)a.B1, (float*)a.C);
+                         (const float*)a.B0, (const float*)a.B1, (float*)a.C, nullptr, nullptr, nullptr, 0);
     else
       hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
                          (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const float*)a.B0, nullptr, (float*)a.C);
+                         (const float*)a.B0, nullptr, (float*)a.C, a.out_tok, a.out_w, a.y_acc, a.T);
   }
   return hipGetLastError();
 }

@@ -59,11 +59,26 @@ struct GroupedGemmArgs {
   const void* B1;       // [G][N][K] (gate/up: the up projection) or null
   void* C;              // [max_rows][N]
   int dtype;
+  // Scatter form (single only): instead of writing C, row r of the product, rounded
+  // to dtype, times out_w[r] is added (fp32 atomics) to y_acc[out_tok[r]] ([T][N]
+  // fp32); rows with out_tok[r] outside [0, T) are skipped.
+  const int32_t* out_tok = nullptr;
+  const float* out_w = nullptr;
+  float* y_acc = nullptr;
+  int T = 0;
 };
 // dual = true: C = SiLU(A B0^T) * (A B1^T); dual = false: C = A B0^T.
 // bf16 launches with max_rows <= kSkinnyRowsPerGroup * G use the skinny kernel.
 constexpr int kSkinnyRowsPerGroup = 16;
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream);
+
+// Around the scatter form of the down GEMM: zero y_acc [T][d] and write
+// row_w[row_of[t][j]] = topk_w[t][j] for kept slots (before); y = y_acc +
+// shared_y, rounded to dtype (after).
+hipError_t launch_scatter_prologue(float* y_acc, float* row_w, const int32_t* row_of, const float* topk_w, int T,
+                                   int k, int d, int max_rows, hipStream_t stream);
+hipError_t launch_scatter_finish(const float* y_acc, const void* shared_y, int dtype, int T, int d, void* y,
+                                 hipStream_t stream);
 
 struct CombineArgs {
   const void* y_perm;

@@ -64,7 +64,7 @@ class Buffers:
     x_perm (the gathered copy of x) is only allocated with ``gathered=True``;
     by default the gate/up GEMM reads x through perm_token."""
 
-    def __init__(self, shape: LayerShape, T: int, device="cuda", gathered: bool = False):
+    def __init__(self, shape: LayerShape, T: int, device="cuda", gathered: bool = False, scatter: bool = False):
         s = shape
         dev = torch.device(device)
         td = torch_dtype(s.dtype)
@@ -91,6 +91,9 @@ class Buffers:
                                       device=dev)
         self.ws_stats = torch.empty((max(_lib.moe_stats_workspace_bytes(T, s.E), 1),), dtype=torch.uint8,
                                     device=dev)
+        # scatter combine: the float32 accumulator and row weights of moe_grouped_down_combine
+        self.ws_scatter = (torch.empty((max(_lib.moe_down_combine_workspace_bytes(T, s.d, R), 1),),
+                                       dtype=torch.uint8, device=dev) if scatter else None)
         # ordering between the main stream and a side stream running the statistics
         self.fork_event, self.stats_event = torch.cuda.Event(), torch.cuda.Event()
         if s.F_shared > 0:
@@ -107,14 +110,19 @@ SMALL_GROUP_ROWS = 16
 
 
 class MoeLayer:
-    """Forward pass of one MoE layer through libmoe.so."""
+    """Forward pass of one MoE layer through libmoe.so.
 
-    def __init__(self, weights: DeviceWeights):
+    scatter_combine: the down GEMM adds its weighted rows straight into a float32
+    accumulator (moe_grouped_down_combine) instead of writing y_perm for the
+    gather combine; y then depends on the order of float32 atomic additions."""
+
+    def __init__(self, weights: DeviceWeights, scatter_combine: bool = False):
         self.w = weights
         self.shape = weights.shape
+        self.scatter_combine = scatter_combine
 
     def buffers(self, T: int, gathered: bool = False) -> Buffers:
-        return Buffers(self.shape, T, self.w.device, gathered)
+        return Buffers(self.shape, T, self.w.device, gathered, scatter=self.scatter_combine)
 
     def route(self, x, b: Buffers, stream=None):
         s = self.shape
@@ -161,6 +169,15 @@ class MoeLayer:
         _lib.moe_grouped_swiglu(x, None, 0, b.shared_offsets, 1, b.T, s.d, s.F_shared, g, u, dn, b.shared_a,
                                 b.shared_y, stream)
 
+    def down_combine(self, b: Buffers, stream=None):
+        """The down GEMM with the combine in its epilogue; adds shared_y, so the
+        shared expert runs first."""
+        s = self.shape
+        if b.ws_scatter is None:
+            raise ValueError("these buffers hold no scatter workspace (Buffers(..., scatter=True))")
+        _lib.moe_grouped_down_combine(b.a, b.offsets, s.E, b.T * s.k, s.F, s.d, self.w.down, b.perm_token, b.row_of,
+                                      b.topk_w, b.T, s.k, b.shared_y, b.y, b.ws_scatter, stream)
+
     def combine(self, b: Buffers, stream=None):
         s = self.shape
         _lib.moe_combine(b.y_perm, b.row_of, b.topk_w, b.shared_y, b.T, s.k, s.d, b.y, stream)
@@ -190,7 +207,9 @@ class MoeLayer:
         more than the overlap saves.  Results are identical either way.
         marks: three events recorded on `stream` before gate/up, between gate/up
         and down, and after down (for timing); a fourth, if given, after the
-        shared expert."""
+        shared expert.  With the scatter combine the order is gate/up, shared
+        expert, down with the combine: the marks then fall before gate/up, after
+        it, after the shared expert and after the down+combine call."""
         if b is None:
             b = self.buffers(x.shape[0])
         if b.T == 0:
@@ -206,6 +225,20 @@ class MoeLayer:
         self.gate_up(x, b, st)
         if marks is not None:
             marks[1].record(st)
+        if b.ws_scatter is not None:
+            self.shared_expert(x, b, st)
+            if marks is not None:
+                marks[2].record(st)
+            if side_stream is not None:
+                self._fork_stats(b, st, side_stream)
+            self.down_combine(b, st)
+            if marks is not None and len(marks) > 3:
+                marks[3].record(st)
+            if side_stream is None:
+                self.stats(b, st)
+            else:
+                st.wait_event(b.stats_event)
+            return b
         self.down(b, st)
         if marks is not None:
             marks[2].record(st)

@@ -50,14 +50,14 @@ class ExpertCache:
 class LayerRun:
     """Upload one layer, run it once through the C ABI, keep host copies."""
 
-    def __init__(self, inp: minp.LayerInputs, device="cuda", gathered: bool = False):
+    def __init__(self, inp: minp.LayerInputs, device="cuda", gathered: bool = False, scatter: bool = False):
         self.inp, self.shape = inp, inp.shape
         s = self.shape
         t0 = time.time()
         self.weights = DeviceWeights(inp, device)
-        self.layer = MoeLayer(self.weights)
+        self.layer = MoeLayer(self.weights, scatter_combine=scatter)
         self.x = to_device(inp.x, s.dtype, device)
-        self.bufs = Buffers(s, s.T, device, gathered)
+        self.bufs = Buffers(s, s.T, device, gathered, scatter=scatter)
         log(f"[{s.name}] uploaded T={s.T} d={s.d} E={s.E} k={s.k} F={s.F} Fs={s.F_shared} in {time.time() - t0:.1f}s")
 
     def run(self):
@@ -91,7 +91,8 @@ def check_route(inp, out, ref=None, select_bias=None):
     chosen keys that are consecutively closer than the gap, where the same
     experts must fill the run's slots and their order follows the kernel's own
     keys (descending, up to their rounding); gate weights, matched by expert,
-    within tolerance.  Logs how many tokens such runs exempt.  Returns the tokens
+    within tolerance.  Logs how many tokens such runs exempt and caps them at
+    max(4, T / 1000).  Returns the tokens
     whose chosen set may differ."""
     s = inp.shape
     sb = inp.select_bias if select_bias is None else select_bias
@@ -114,6 +115,9 @@ def check_route(inp, out, ref=None, select_bias=None):
     reordered = int((out["idx"][ok] != idx[ok]).any(1).sum())
     close_tokens = int(close[ok].any(1).sum())
     assert reordered <= close_tokens
+    # a bound on the exemption itself: runs of keys within 1e-4 are rare in these
+    # inputs (at most one reordered token in any workload here)
+    assert reordered <= max(4, s.T // 1000), f"{reordered} tokens reordered inside near-equal runs"
     own_keys = oracle.selection_keys(out["scores"], s.mode, sb).astype(np.float64)
     own = np.take_along_axis(own_keys, out["idx"].astype(np.int64), 1)
     slack = 0.0 if (sb is None and s.mode != oracle.SIGMOID_THEN_TOPK) else 1e-6
@@ -163,3 +167,18 @@ def check_stats(inp, out, scores_gpu=None):
 
 def max_rel(a, ref):
     return float(np.abs(np.asarray(a, np.float64) - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def assert_same_sum(y_a, y_b, dtype, what=""):
+    """Two results of one float32 sum taken in different orders, each rounded once
+    to dtype: bf16 values at most one unit in the last place apart (2^-7 of the
+    value), plus 1e-5 of the row's largest value where the sum cancels.  Returns
+    the fraction of elements that differ at all."""
+    y_a, y_b = np.asarray(y_a, np.float64), np.asarray(y_b, np.float64)
+    m = np.maximum(np.abs(y_a), np.abs(y_b))
+    rowmax = np.abs(y_b).max(axis=-1, keepdims=True)
+    rel = 2.0 ** -7 if dtype == "bf16" else 1e-6
+    bound = rel * m + 1e-5 * rowmax
+    bad = np.abs(y_a - y_b) > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond one rounding apart"
+    return float((y_a != y_b).mean())

@@ -187,3 +187,33 @@ def test_permute_noalloc_rejects_beyond_its_scratch_before_launch():
     assert "scratch" in _lib.last_error()
     assert lib.moe_permute_noalloc(8, 0, k, E, -1, 0, _lib.MOE_BF16, 128, 8, 8, 8, 8, 0, 0) == _lib.MOE_OK
     assert lib.moe_permute_noalloc(0, 16, k, E, -1, 0, _lib.MOE_BF16, 128, 8, 8, 8, 8, 0, 0) == _lib.MOE_ERR_INVALID_ARG
+
+
+def test_down_combine_rejects_before_launch():
+    """moe_grouped_down_combine checks sizes, pointers and its workspace on the host;
+    T = 0 is a no-op."""
+    lib = _lib.load()
+    T, k, d, F, G = 16, 2, 128, 256, 4
+    R = T * k
+    need = _lib.moe_down_combine_workspace_bytes(T, d, R)
+    assert need >= T * d * 4 + R * 4
+    assert _lib.moe_down_combine_workspace_bytes(-1, d, R) == 0
+
+    def call(**kw):
+        a = dict(a=FAKE, off=FAKE, G=G, rows=R, F=F, d=d, w=FAKE, dt=_lib.MOE_BF16, pt=FAKE, ro=FAKE, tw=FAKE, T=T,
+                 k=k, sh=None, y=FAKE, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.moe_grouped_down_combine(a["a"], a["off"], a["G"], a["rows"], a["F"], a["d"], a["w"], a["dt"],
+                                            a["pt"], a["ro"], a["tw"], a["T"], a["k"], a["sh"], a["y"], a["ws"],
+                                            a["wsb"], None)
+
+    assert call(wsb=need - 1) == _lib.MOE_ERR_WORKSPACE
+    assert call(ws=None) == _lib.MOE_ERR_WORKSPACE
+    assert call(T=-1) == _lib.MOE_ERR_INVALID_ARG
+    assert call(k=0) == _lib.MOE_ERR_INVALID_ARG
+    assert call(y=None) == _lib.MOE_ERR_INVALID_ARG
+    assert call(pt=None) == _lib.MOE_ERR_INVALID_ARG
+    assert call(d=100) == _lib.MOE_ERR_UNSUPPORTED
+    assert call(G=0) == _lib.MOE_ERR_INVALID_ARG
+    assert call(dt=7) == _lib.MOE_ERR_INVALID_ARG
+    assert call(T=0, a=None, off=None, w=None, pt=None, ro=None, tw=None, y=None, ws=None, wsb=0) == _lib.MOE_OK

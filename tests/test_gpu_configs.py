@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from mixture_experts_ffn_08_amd import inputs as minp
-from support import TOL, ExpertCache, LayerRun, check_dispatch, check_route, check_stats, host, log, oracle_route
+from support import TOL, ExpertCache, LayerRun, assert_same_sum, check_dispatch, check_route, check_stats, host, \
+    log, oracle_route
 
 pytestmark = pytest.mark.gpu
 
@@ -133,5 +134,30 @@ def test_config_parity(name):
         log(f"[{name}] {len(toks)} tokens from the definition agree with the accumulated oracle to {d_err:.1e}; "
             f"total {time.time() - t0:.1f}s")
         assert d_err <= 1e-9 * ymax
+    finally:
+        run.free()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_skew", "mixtral_cap", "qwen3_decode"])
+def test_scatter_combine_full_size(name):
+    """At full size, in the launch configuration of the timed layer: the scatter
+    combine (weighted sum in the down GEMM's epilogue) against the gather combine,
+    y one rounding of the same sum apart on every token.  The gather path's y is
+    compared with the oracle in full by test_config_parity."""
+    shape = minp.SHAPES[name]
+    inp = minp.LayerInputs(shape, seed=0)
+    run = LayerRun(inp)
+    try:
+        ref = run.run()["y"]
+        lay = run.layer
+        lay.scatter_combine = True
+        run.bufs = type(run.bufs)(shape, shape.T, "cuda", scatter=True)
+        run.bufs.y.fill_(float("nan"))
+        out = run.run()
+        assert np.isfinite(out["y"]).all()
+        frac = assert_same_sum(out["y"], ref, shape.dtype, name)
+        log(f"[{name}] scatter combine at full size: {100 * frac:.3f}% of y differs from the gather combine "
+            f"(within one rounding)")
     finally:
         run.free()

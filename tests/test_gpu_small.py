@@ -13,7 +13,8 @@ from mixture_experts_ffn_08_amd import _lib
 from mixture_experts_ffn_08_amd import inputs as minp
 from mixture_experts_ffn_08_amd.inputs import SIGMOID_THEN_TOPK as SIG, SOFTMAX_THEN_TOPK as SM_TK, \
     TOPK_THEN_SOFTMAX as TK_SM
-from support import TOL, ExpertCache, LayerRun, check_dispatch, check_route, check_stats, host, log, max_rel
+from support import TOL, ExpertCache, LayerRun, assert_same_sum, check_dispatch, check_route, check_stats, host, \
+    log, max_rel
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +58,10 @@ SMALL = [
     S("many_tokens_E128_topk_first_zipf", "bf16", 2300, 384, 128, 8, 128, 0, TK_SM, False, None, True),
     S("many_tokens_E72_softmax_biased", "bf16", 2051, 1152, 72, 8, 128, 0, SM_TK, False, None, False,
       select_bias=0.01),
+    # ... and from T = 4096 on, 64-token blocks on 8 waves (ragged last block)
+    S("many_tokens_E96_wide_sigmoid_biased", "bf16", 4133, 256, 96, 6, 128, 0, SIG, False, None, False,
+      select_bias=0.05),
+    S("many_tokens_E128_wide_softmax_renorm", "bf16", 4097, 384, 128, 8, 128, 0, SM_TK, True, None, False),
     # E = 256 with T (E / 64) past the split-score limit: the fused kernel with 256 experts
     S("many_tokens_E256_fused", "bf16", 8300, 128, 256, 8, 128, 0, SM_TK, True, None, True, select_bias=0.002),
 ]
@@ -144,6 +149,49 @@ def test_materialized_gather_matches_fused(idx):
         full_check(inp, out)
     finally:
         run_state.clear()
+        run.free()
+
+
+SCATTER_CASES = ["small_renorm", "small_shared", "small_capacity", "small_zipf", "tiny_f32", "f32_ragged",
+                 "one_token", "E256", "k_over_64", "many_tokens", "many_tokens_E128_d640"]
+
+
+@pytest.mark.parametrize("name", SCATTER_CASES)
+def test_scatter_combine_matches_gather(name):
+    """The down GEMM with the weighted sum in its epilogue (float32 atomics into an
+    accumulator, then + shared expert, one rounding) against the down GEMM writing
+    y_perm and the gather combine: routing, dispatch and statistics bit-identical,
+    y one rounding of the same sum apart (tiled, skinny and float32 GEMM kernels,
+    the shared expert, dropped slots, k > 64), twice in a row on one workspace;
+    and y against the oracle's whole layer."""
+    shape = next(s for s in SMALL if s.name == name)
+    inp = minp.LayerInputs(shape, seed=5)
+    g = LayerRun(inp)
+    ref = g.run()
+    g.free()
+    run = LayerRun(inp, scatter=True)
+    try:
+        s = shape
+        R = int(ref["offsets"][-1])
+        for rep in range(2):
+            out = run.run()
+            for key in ("scores", "idx", "w", "near_tie", "counts", "offsets", "row_of", "f", "P", "l_aux",
+                        "max_over_mean"):
+                assert np.array_equal(np.asarray(out[key]), np.asarray(ref[key])), key
+            assert np.array_equal(out["perm_token"][:R], ref["perm_token"][:R])
+            frac = assert_same_sum(out["y"], ref["y"], s.dtype, f"{name} call {rep}")
+            log(f"[{name}] scatter combine, call {rep}: {100 * frac:.3f}% of y differs from the gather combine "
+                f"(within one rounding)")
+        ex = ExpertCache(inp)
+        xs = minp.as_f32(inp.x, s.dtype)
+        full = oracle.layer_forward(xs, minp.as_f32(inp.w_router, s.dtype), inp.bias, ex, ex.shared(), k=s.k,
+                                    mode=s.mode, renorm=s.renorm, phi=s.phi, alpha=s.alpha, dtype=s.dtype,
+                                    select_bias=inp.select_bias)
+        same = ~(out["idx"] != full["idx"]).any(1) & ~((out["near_tie"] == 1) | (full["near_tie"] == 1))
+        if same.any():
+            err = np.abs(out["y"][same] - full["y64"][same]).max()
+            assert err <= TOL[s.dtype] * np.abs(full["y64"]).max()
+    finally:
         run.free()
 
 
@@ -278,6 +326,13 @@ def test_padded_layout_layer_matches_compact(shape):
     _lib.moe_combine(yp, b.row_of, b.topk_w, b.shared_y if s.F_shared else None, s.T, s.k, s.d, y, y_rows=slots)
     torch.cuda.synchronize()
     assert np.array_equal(host(y), y_compact)
+    # the scatter combine over the padded slots (padding slots hold token -1)
+    ws = torch.empty(_lib.moe_down_combine_workspace_bytes(s.T, s.d, slots), dtype=torch.uint8, device="cuda")
+    y_sc = torch.empty((s.T, s.d), dtype=torch.bfloat16, device="cuda")
+    _lib.moe_grouped_down_combine(a, b.offsets, s.E, slots, s.F, s.d, w.down, slot, b.row_of, b.topk_w, s.T, s.k,
+                                  b.shared_y if s.F_shared else None, y_sc, ws)
+    torch.cuda.synchronize()
+    assert_same_sum(host(y_sc), y_compact, s.dtype, "padded scatter combine")
     ex = ExpertCache(inp)
     full = oracle.layer_forward(minp.as_f32(inp.x, s.dtype), minp.as_f32(inp.w_router, s.dtype), inp.bias, ex,
                                 ex.shared(), k=s.k, mode=s.mode, renorm=s.renorm, phi=s.phi, alpha=s.alpha,
