@@ -351,6 +351,77 @@ int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, f
 
 size_t moe_stats_workspace_bytes(int T, int E);
 
+/*
+ * moe_layer_forward -- the whole layer in one call: moe_route, moe_permute
+ * (compact layout, no x_perm), moe_grouped_gate_up (rows gathered through
+ * perm_token), moe_grouped_down, the shared expert (moe_grouped_swiglu with
+ * G = 1, when F_shared > 0), moe_combine and moe_stats, in that order, with the
+ * arguments of the struct below.  Every call's checks run first; on a bad
+ * argument nothing is enqueued and the status and moe_last_error() are those of
+ * the first call that rejects it.
+ * With bf16, T <= 64 and T k <= 512 (decode batches) the selection, the
+ * dispatch and the statistics run as one block after the score kernel, with no
+ * launch between them: the results are bit-identical to the separate calls.
+ * Sources: the five steps as each call cites them; Transformers & Math 17.2
+ * equation for the layer sum.
+ *
+ * Every pointer is a device pointer, with the shape and meaning given for the
+ * call that takes it; R = T k.
+ */
+typedef struct moe_layer_args {
+  int dtype, T, d, E, k, F;
+  int F_shared;                 /* 0: no shared expert */
+  int mode, renorm;             /* as for moe_route */
+  int64_t capacity;             /* moe_capacity(T, k, E, phi), < 0: dropless */
+  float alpha;                  /* L_aux coefficient */
+  const void* x;                /* [T][d] */
+  const void* w_router;         /* [E][d] */
+  const float* logit_bias;      /* [E] or NULL */
+  const float* select_bias;     /* [E] or NULL */
+  const void* w_gate;           /* [E][F][d] */
+  const void* w_up;             /* [E][F][d] */
+  const void* w_down;           /* [E][d][F] */
+  const void* shared_gate;      /* [F_shared][d], with F_shared > 0 */
+  const void* shared_up;        /* [F_shared][d] */
+  const void* shared_down;      /* [d][F_shared] */
+  const int32_t* shared_offsets;  /* [2] = {0, T}, with F_shared > 0 */
+  float* logits;                /* [T][E] out */
+  int32_t* topk_idx;            /* [T][k] out */
+  float* topk_w;                /* [T][k] out */
+  int32_t* near_tie;            /* [T] out */
+  int32_t* counts;              /* [E] out */
+  int32_t* offsets;             /* [E+1] out */
+  int32_t* row_of;              /* [T][k] out */
+  int32_t* perm_token;          /* [R] out */
+  void* a;                      /* [R][F] out */
+  void* y_perm;                 /* [R][d] out */
+  void* shared_a;               /* [T][F_shared] out, with F_shared > 0 */
+  void* shared_y;               /* [T][d] out, with F_shared > 0 */
+  void* y;                      /* [T][d] out */
+  float* f;                     /* [E] out */
+  float* P;                     /* [E] out */
+  float* l_aux;                 /* [1] out */
+  float* max_over_mean;         /* [1] out */
+  void* permute_workspace;      /* >= moe_permute_workspace_bytes(T, k, E) */
+  size_t permute_workspace_bytes;
+  void* stats_workspace;        /* >= moe_stats_workspace_bytes(T, E) */
+  size_t stats_workspace_bytes;
+  /* Optional: with side_stream, fork_event and join_event all given (and not
+   * the decode form above), the statistics run on side_stream after the work
+   * before the combine, and `stream` waits for them before the call returns
+   * its last operation.  The events are the caller's (hipEventCreate...). */
+  hipStream_t side_stream;
+  hipEvent_t fork_event;
+  hipEvent_t join_event;
+  /* Optional timing marks, each recorded on `stream` if not NULL: before the
+   * gate/up GEMM, after it, after the down GEMM, after the shared expert. */
+  hipEvent_t marks[4];
+} moe_layer_args;
+
+int moe_layer_forward(const moe_layer_args* args, hipStream_t stream);
+/* sizeof(moe_layer_args), for bindings that lay the struct out themselves. */
+size_t moe_layer_args_size(void);
+
 /* Human-readable name of a moe_status value. */
 const char* moe_status_string(int status);
 

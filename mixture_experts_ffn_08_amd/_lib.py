@@ -24,12 +24,34 @@ MOE_MAX_EXPERTS = 256
 EXPORTS = ("moe_route", "moe_bias_update", "moe_permute", "moe_permute_noalloc", "moe_permute_padded",
            "moe_permute_workspace_bytes", "moe_capacity",
            "moe_grouped_gate_up", "moe_grouped_down", "moe_grouped_swiglu", "moe_combine",
-           "moe_grouped_down_combine", "moe_down_combine_workspace_bytes", "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
+           "moe_grouped_down_combine", "moe_down_combine_workspace_bytes", "moe_layer_forward",
+           "moe_layer_args_size", "moe_stats", "moe_stats_workspace_bytes", "moe_status_string", "moe_last_error")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
+class MoeLayerArgs(ctypes.Structure):
+    """moe_layer_args of include/moe.h, field for field (the C layout rules of
+    this platform; moe_layer_args_size() must equal ctypes.sizeof of it)."""
+    _fields_ = [
+        ("dtype", _I), ("T", _I), ("d", _I), ("E", _I), ("k", _I), ("F", _I), ("F_shared", _I),
+        ("mode", _I), ("renorm", _I), ("capacity", _I64), ("alpha", ctypes.c_float),
+        ("x", _P), ("w_router", _P), ("logit_bias", _P), ("select_bias", _P),
+        ("w_gate", _P), ("w_up", _P), ("w_down", _P),
+        ("shared_gate", _P), ("shared_up", _P), ("shared_down", _P), ("shared_offsets", _P),
+        ("logits", _P), ("topk_idx", _P), ("topk_w", _P), ("near_tie", _P),
+        ("counts", _P), ("offsets", _P), ("row_of", _P), ("perm_token", _P),
+        ("a", _P), ("y_perm", _P), ("shared_a", _P), ("shared_y", _P), ("y", _P),
+        ("f", _P), ("P", _P), ("l_aux", _P), ("max_over_mean", _P),
+        ("permute_workspace", _P), ("permute_workspace_bytes", _SZ),
+        ("stats_workspace", _P), ("stats_workspace_bytes", _SZ),
+        ("side_stream", _P), ("fork_event", _P), ("join_event", _P),
+        ("marks", _P * 4),
+    ]
+
+
+
 _SIGS = {
     "moe_route": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "moe_bias_update": (_I, [_P, _I, _I, _I, ctypes.c_float, _P, _P]),
@@ -44,11 +66,15 @@ _SIGS = {
     "moe_combine": (_I, [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
     "moe_grouped_down_combine": (_I, [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _I, _I, _P, _P, _P, _SZ, _P]),
     "moe_down_combine_workspace_bytes": (_SZ, [_I, _I, _I]),
+    "moe_layer_forward": (_I, [ctypes.POINTER(MoeLayerArgs), _P]),
+    "moe_layer_args_size": (_SZ, []),
     "moe_stats": (_I, [_P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_stats_workspace_bytes": (_SZ, [_I, _I]),
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_last_error": (ctypes.c_char_p, []),
 }
+
+
 
 _lib = None
 
@@ -265,6 +291,78 @@ def moe_grouped_down_combine(a, offsets, G, max_rows, F, d, w_down, perm_token, 
             _dev(shared_y, "shared_y", y.dtype, T * d, optional=True), _dev(y, "y", y.dtype, T * d),
             _dev(workspace, "workspace"), ws_bytes, _stream(stream))
     _check("moe_grouped_down_combine", load().moe_grouped_down_combine(*args))
+
+
+def _event(ev, stream):
+    """The HIP event of a torch event (None for None).  torch creates the event on
+    its first record, so an event without one is recorded here first; the
+    library's later record is the one that counts."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record(stream if stream is not None else torch.cuda.current_stream())
+    return ev.cuda_event
+
+
+def layer_args(shape, x, weights, bufs, capacity) -> MoeLayerArgs:
+    """The moe_layer_args of one layer call: every tensor checked (device, dtype,
+    contiguity, size) as the single calls check them, then its address.  The
+    struct can be kept and passed again while the tensors live."""
+    s, T, w, b = shape, bufs.T, weights, bufs
+    td, R = x.dtype, T * shape.k
+    i32, f32 = torch.int32, torch.float32
+    a = MoeLayerArgs()
+    a.dtype, a.T, a.d, a.E, a.k, a.F = _dtype_code(x), T, s.d, s.E, s.k, s.F
+    a.F_shared = s.F_shared if w.shared is not None else 0
+    a.mode, a.renorm, a.capacity, a.alpha = s.mode, int(bool(s.renorm)), int(capacity), float(s.alpha)
+    a.x = _dev(x, "x", td, T * s.d)
+    a.w_router = _dev(w.w_router, "w_router", td, s.E * s.d)
+    a.logit_bias = _dev(w.bias, "bias", f32, s.E, optional=True)
+    a.select_bias = _dev(w.select_bias, "select_bias", f32, s.E, optional=True)
+    a.w_gate = _dev(w.gate, "w_gate", td, s.E * s.F * s.d)
+    a.w_up = _dev(w.up, "w_up", td, s.E * s.F * s.d)
+    a.w_down = _dev(w.down, "w_down", td, s.E * s.d * s.F)
+    if a.F_shared:
+        g, u, dn = w.shared
+        a.shared_gate = _dev(g, "shared_gate", td, a.F_shared * s.d)
+        a.shared_up = _dev(u, "shared_up", td, a.F_shared * s.d)
+        a.shared_down = _dev(dn, "shared_down", td, s.d * a.F_shared)
+        a.shared_offsets = _dev(b.shared_offsets, "shared_offsets", i32, 2)
+        a.shared_a = _dev(b.shared_a, "shared_a", td, T * a.F_shared)
+        a.shared_y = _dev(b.shared_y, "shared_y", td, T * s.d)
+    a.logits = _dev(b.logits, "logits", f32, T * s.E)
+    a.topk_idx = _dev(b.topk_idx, "topk_idx", i32, R)
+    a.topk_w = _dev(b.topk_w, "topk_w", f32, R)
+    a.near_tie = _dev(b.near_tie, "near_tie", i32, T)
+    a.counts = _dev(b.counts, "counts", i32, s.E)
+    a.offsets = _dev(b.offsets, "offsets", i32, s.E + 1)
+    a.row_of = _dev(b.row_of, "row_of", i32, R)
+    a.perm_token = _dev(b.perm_token, "perm_token", i32, R)
+    a.a = _dev(b.a, "a", td, R * s.F)
+    a.y_perm = _dev(b.y_perm, "y_perm", td, R * s.d)
+    a.y = _dev(b.y, "y", td, T * s.d)
+    a.f = _dev(b.f, "f", f32, s.E)
+    a.P = _dev(b.P, "P", f32, s.E)
+    a.l_aux = _dev(b.l_aux, "l_aux", f32, 1)
+    a.max_over_mean = _dev(b.max_over_mean, "max_over_mean", f32, 1)
+    a.permute_workspace = _dev(b.ws_permute, "permute_workspace")
+    a.permute_workspace_bytes = b.ws_permute.numel() * b.ws_permute.element_size()
+    a.stats_workspace = _dev(b.ws_stats, "stats_workspace")
+    a.stats_workspace_bytes = b.ws_stats.numel() * b.ws_stats.element_size()
+    return a
+
+
+def moe_layer_forward(args: MoeLayerArgs, stream=None, side_stream=None, fork_event=None, join_event=None,
+                      marks=None):
+    """One layer through moe_layer_forward.  side_stream / fork_event / join_event
+    (torch objects, events already recorded once) run the statistics beside the
+    combine; marks: up to four recorded torch events for timing."""
+    args.side_stream = _stream(side_stream) if side_stream is not None else None
+    args.fork_event = _event(fork_event, stream)
+    args.join_event = _event(join_event, stream)
+    for i in range(4):
+        args.marks[i] = _event(marks[i], stream) if marks is not None and i < len(marks) else None
+    _check("moe_layer_forward", load().moe_layer_forward(ctypes.byref(args), _stream(stream)))
 
 
 def moe_stats(counts, logits, T, k, E, alpha, f, P, l_aux, max_over_mean, workspace, stream=None):

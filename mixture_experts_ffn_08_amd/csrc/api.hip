@@ -14,6 +14,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+// Set by moe_layer_forward while it runs every call's checks: the entry points
+// then return after their checks, before enqueueing anything.
+thread_local bool g_check_only = false;
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -147,6 +150,7 @@ int moe_route(const void* x, const void* w_router, const float* logit_bias, cons
   NEED(topk_idx, fn);
   NEED(topk_w, fn);
   NEED(near_tie, fn);
+  if (g_check_only) return ok();
   moe::RouteArgs a{x, w_router, logit_bias, select_bias, dtype, T, d, E, k, mode, renorm ? 1 : 0,
                    logits, topk_idx, topk_w, near_tie};
   return hip_status(moe::launch_route(a, stream), fn);
@@ -207,6 +211,7 @@ int moe_permute(const int32_t* topk_idx, int T, int k, int E, int64_t capacity, 
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
+  if (g_check_only) return ok();
   const size_t half = need / 2;
   moe::PermuteArgs a{topk_idx, T, k, E, capacity < 0 ? -1 : capacity, x, d * elem_bytes(dtype), counts,
                      offsets, row_of, perm_token, x_perm, static_cast<int32_t*>(workspace),
@@ -340,6 +345,7 @@ int moe_grouped_gate_up(const void* x, const int32_t* row_index, int src_rows, c
   NEED(w_gate, fn);
   NEED(w_up, fn);
   NEED(a, fn);
+  if (g_check_only) return ok();
   moe::GroupedGemmArgs g{x, row_index, row_index ? src_rows : max_rows, offsets, G, max_rows, F, d,
                          w_gate, w_up, a, dtype};
   return hip_status(moe::launch_grouped_gemm(g, true, stream), fn);
@@ -354,6 +360,7 @@ int moe_grouped_down(const void* a, const int32_t* offsets, int G, int max_rows,
   NEED(offsets, fn);
   NEED(w_down, fn);
   NEED(y_perm, fn);
+  if (g_check_only) return ok();
   moe::GroupedGemmArgs g{a, nullptr, max_rows, offsets, G, max_rows, d, F, w_down, nullptr, y_perm, dtype};
   return hip_status(moe::launch_grouped_gemm(g, false, stream), fn);
 }
@@ -386,6 +393,7 @@ int moe_combine(const void* y_perm, int y_rows, const int32_t* row_of, const flo
   NEED(row_of, fn);
   NEED(topk_w, fn);
   NEED(y, fn);
+  if (g_check_only) return ok();
   moe::CombineArgs c{y_perm, row_of, topk_w, shared_y, dtype, T, k, d, y_rows, y};
   return hip_status(moe::launch_combine(c, stream), fn);
 }
@@ -436,6 +444,84 @@ int moe_grouped_down_combine(const void* a, const int32_t* offsets, int G, int m
   return hip_status(moe::launch_scatter_finish(y_acc, shared_y, dtype, T, d, y, stream), fn);
 }
 
+size_t moe_layer_args_size(void) { return sizeof(moe_layer_args); }
+
+}  // extern "C"
+
+namespace {
+
+// The layer's calls in order on `stream` (route and permute, or their fused
+// decode form, then the GEMMs, the shared expert, the combine and the
+// statistics).  `check` runs every call's checks and enqueues nothing.
+int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
+  const int64_t R = (int64_t)L.T * L.k;
+  const bool fused = moe::route_dispatch_small_fits(L.dtype, L.T, L.k, L.E);
+  auto mark = [&](int i) -> int {
+    if (check || L.marks[i] == nullptr) return MOE_OK;
+    return hip_status(hipEventRecord(L.marks[i], stream), "moe_layer_forward");
+  };
+  if (check || !fused) {
+    CHECK(moe_route(L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode, L.renorm,
+                    L.logits, L.topk_idx, L.topk_w, L.near_tie, stream));
+    CHECK(moe_permute(L.topk_idx, L.T, L.k, L.E, L.capacity, L.x, L.dtype, L.d, L.counts, L.offsets, L.row_of,
+                      L.perm_token, nullptr, L.permute_workspace, L.permute_workspace_bytes, stream));
+  }
+  if (!check && fused) {
+    moe::RouteDispatchArgs a{{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,
+                              L.renorm ? 1 : 0, L.logits, L.topk_idx, L.topk_w, L.near_tie},
+                             L.capacity < 0 ? -1 : L.capacity, L.counts, L.offsets, L.row_of, L.perm_token,
+                             L.alpha, L.f, L.P, L.l_aux, L.max_over_mean};
+    CHECK(hip_status(moe::launch_route_dispatch_small(a, stream), "moe_layer_forward"));
+  }
+  CHECK(mark(0));
+  CHECK(moe_grouped_gate_up(L.x, L.perm_token, L.T, L.offsets, L.E, (int)R, L.d, L.F, L.w_gate, L.w_up, L.dtype,
+                            L.a, stream));
+  CHECK(mark(1));
+  CHECK(moe_grouped_down(L.a, L.offsets, L.E, (int)R, L.F, L.d, L.w_down, L.dtype, L.y_perm, stream));
+  CHECK(mark(2));
+  if (L.F_shared > 0)
+    CHECK(moe_grouped_swiglu(L.x, nullptr, 0, L.shared_offsets, 1, L.T, L.d, L.F_shared, L.shared_gate,
+                             L.shared_up, L.shared_down, L.dtype, L.shared_a, L.shared_y, stream));
+  CHECK(mark(3));
+  const bool side = !fused && L.side_stream != nullptr && L.fork_event != nullptr && L.join_event != nullptr;
+  auto stats = [&](hipStream_t st) {
+    return moe_stats(L.counts, L.logits, L.T, L.k, L.E, L.alpha, L.f, L.P, L.l_aux, L.max_over_mean,
+                     L.stats_workspace, L.stats_workspace_bytes, st);
+  };
+  if (side && !check) {
+    CHECK(hip_status(hipEventRecord(L.fork_event, stream), "moe_layer_forward"));
+    CHECK(hip_status(hipStreamWaitEvent(L.side_stream, L.fork_event, 0), "moe_layer_forward"));
+    CHECK(stats(L.side_stream));
+    CHECK(hip_status(hipEventRecord(L.join_event, L.side_stream), "moe_layer_forward"));
+  }
+  CHECK(moe_combine(L.y_perm, (int)R, L.row_of, L.topk_w, L.F_shared > 0 ? L.shared_y : nullptr, L.dtype, L.T, L.k,
+                    L.d, L.y, stream));
+  if (side && !check) return hip_status(hipStreamWaitEvent(stream, L.join_event, 0), "moe_layer_forward");
+  if (check || !fused) CHECK(stats(stream));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_forward(const moe_layer_args* args, hipStream_t stream) {
+  static const char* fn = "moe_layer_forward";
+  if (args == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s: args must not be NULL", fn);
+  const moe_layer_args& L = *args;
+  if (L.T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %d < 0", fn, L.T);
+  if (L.F_shared < 0) return fail(MOE_ERR_INVALID_ARG, "%s: F_shared = %d < 0", fn, L.F_shared);
+  if (L.T == 0) return ok();
+  if (L.F_shared > 0) NEED(L.shared_offsets, fn);
+  if ((int64_t)L.T * L.k > INT32_MAX)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: T*k = %lld exceeds 2^31-1", fn, (long long)L.T * L.k);
+  g_check_only = true;
+  const int checked = layer_calls(L, stream, true);
+  g_check_only = false;
+  if (checked != MOE_OK) return checked;
+  return layer_calls(L, stream, false);
+}
+
 int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, float alpha, float* f, float* P,
               float* l_aux, float* max_over_mean, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
@@ -455,6 +541,7 @@ int moe_stats(const int32_t* counts, const float* logits, int T, int k, int E, f
   if (workspace == nullptr || workspace_bytes < need)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
                 workspace ? workspace_bytes : (size_t)0, need);
+  if (g_check_only) return ok();
   moe::StatsArgs s{counts, logits, T, k, E, alpha, f, P, l_aux, max_over_mean, static_cast<float*>(workspace)};
   return hip_status(moe::launch_stats(s, stream), fn);
 }

@@ -1,0 +1,71 @@
+// Dispatch of at most 512 assignments in one block: histogram, capacity, scan over
+// experts and ranks, with the results of the multi-block kernels (per-expert
+// bitmaps of the assignments, ranks by popcount of the earlier bits: fixed by the
+// data, not by the order of the atomics).
+//
+// ML Interview Notes, MoELayer listing (each expert collects the pairs that chose
+// it); "Capacity factor" and Transformers & Math 17.5 (an expert keeps at most C,
+// later arrivals are dropped).
+#pragma once
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+
+constexpr int kSingleMaxPairs = 512;             // assignments one block dispatches
+constexpr int kSingleWords = kSingleMaxPairs / 32;  // bitmap words per expert
+
+// Called by every thread of a block of at least kSingleMaxPairs threads; P <= 512.
+__device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t P, int k, int E, int64_t cap,
+                                       int padded, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                       int32_t* __restrict__ row_of, int32_t* __restrict__ perm_token) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS * kSingleWords];
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  __shared__ int kept[MOE_MAX_EXPERTS];
+  __shared__ int incl[2][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int i = tid; i < E * kSingleWords; i += nthr) mask[i] = 0u;
+  for (int i = tid; i < E; i += nthr) cnt[i] = 0;
+  __syncthreads();
+  const int e = tid < P ? idx[tid] : -1;
+  const bool valid = (unsigned)e < (unsigned)E;
+  const int w = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid) {
+    atomicOr(&mask[e * kSingleWords + w], bit);
+    atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < E; i += nthr) {
+    counts[i] = cnt[i];
+    kept[i] = cap < 0 ? cnt[i] : (int)min((int64_t)cnt[i], cap);
+    incl[0][i] = kept[i];
+  }
+  __syncthreads();
+  // inclusive scan of the kept counts over experts (Hillis-Steele, ping-pong buffers)
+  int src = 0;
+  for (int h = 1; h < E; h <<= 1) {
+    for (int i = tid; i < E; i += nthr) incl[src ^ 1][i] = incl[src][i] + (i >= h ? incl[src][i - h] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  if (!padded) {
+    for (int i = tid; i < E; i += nthr) offsets[i + 1] = incl[src][i];
+    if (tid == 0) offsets[0] = 0;
+  }
+  if (tid >= P) return;
+  int32_t row = -1;
+  if (valid) {
+    const uint32_t* m = mask + e * kSingleWords;
+    int rank = __popc(m[w] & (bit - 1u));
+    for (int q = 0; q < w; ++q) rank += __popc(m[q]);
+    if (cap < 0 || rank < cap) {
+      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept[e] + rank;
+      perm_token[row] = tid / k;
+    }
+  }
+  row_of[tid] = row;
+}
+
+}  // namespace moe

@@ -23,6 +23,19 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
+// Few tokens (bf16, T <= 64, T k <= 512): the scores, then selection, the compact
+// dispatch and the balance statistics in one block (the results of launch_route,
+// launch_permute with capacity and no x_perm, and launch_stats).
+struct RouteDispatchArgs {
+  RouteArgs route;
+  int64_t capacity;  // < 0: dropless
+  int32_t *counts, *offsets, *row_of, *perm_token;
+  float alpha;
+  float *f, *P, *l_aux, *max_over_mean;
+};
+bool route_dispatch_small_fits(int dtype, int T, int k, int E);
+hipError_t launch_route_dispatch_small(const RouteDispatchArgs& a, hipStream_t stream);
+
 // b_e += rate * sign(T k - E counts_e) for e < E.
 hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* bias,
                               hipStream_t stream);

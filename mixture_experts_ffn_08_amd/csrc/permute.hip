@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "dispatch_single.h"
 #include "kernels.h"
 
 namespace moe {
@@ -185,58 +186,14 @@ __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
 
 // All of histogram, scan and rank in one block, for T k <= 512 assignments (the
 // decode shapes): the same results as the three kernels above with one block.
+static_assert(kBP == kSingleMaxPairs, "one thread per assignment");
 __global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __restrict__ idx, int64_t P, int k,
                                                               int E, int64_t cap, int padded,
                                                               int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ row_of,
                                                               int32_t* __restrict__ perm_token) {
-  __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
-  __shared__ int cnt[MOE_MAX_EXPERTS];
-  __shared__ int kept[MOE_MAX_EXPERTS];
-  __shared__ int incl[2][MOE_MAX_EXPERTS];
-  const int tid = threadIdx.x;
-  for (int i = tid; i < E * kWords; i += kBP) mask[i] = 0u;
-  for (int i = tid; i < E; i += kBP) cnt[i] = 0;
-  __syncthreads();
-  const int e = tid < P ? idx[tid] : -1;
-  const bool valid = (unsigned)e < (unsigned)E;
-  const int w = tid >> 5;
-  const uint32_t bit = 1u << (tid & 31);
-  if (valid) {
-    atomicOr(&mask[e * kWords + w], bit);
-    atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  for (int i = tid; i < E; i += kBP) {
-    counts[i] = cnt[i];
-    kept[i] = cap < 0 ? cnt[i] : (int)min((int64_t)cnt[i], cap);
-    incl[0][i] = kept[i];
-  }
-  __syncthreads();
-  // inclusive scan of the kept counts over experts (Hillis-Steele, ping-pong buffers)
-  int src = 0;
-  for (int h = 1; h < E; h <<= 1) {
-    for (int i = tid; i < E; i += kBP) incl[src ^ 1][i] = incl[src][i] + (i >= h ? incl[src][i - h] : 0);
-    __syncthreads();
-    src ^= 1;
-  }
-  if (!padded) {
-    for (int i = tid; i < E; i += kBP) offsets[i + 1] = incl[src][i];
-    if (tid == 0) offsets[0] = 0;
-  }
-  if (tid >= P) return;
-  int32_t row = -1;
-  if (valid) {
-    const uint32_t* m = mask + e * kWords;
-    int rank = __popc(m[w] & (bit - 1u));
-    for (int q = 0; q < w; ++q) rank += __popc(m[q]);
-    if (cap < 0 || rank < cap) {
-      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept[e] + rank;
-      perm_token[row] = tid / k;
-    }
-  }
-  row_of[tid] = row;
+  dispatch_single(idx, P, k, E, cap, padded, counts, offsets, row_of, perm_token);
 }
 
 }  // namespace

@@ -34,7 +34,9 @@
 #include <type_traits>
 
 #include "common.h"
+#include "dispatch_single.h"
 #include "kernels.h"
+#include "stats_single.h"
 
 namespace moe {
 namespace {
@@ -581,6 +583,26 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int E, int k, 
                                                   nullptr, topk_idx, topk_w, near_tie);
 }
 
+// Few tokens: after route_scores_split_kernel, one block of 16 waves selects for
+// all T <= 64 tokens (one token per 16-lane row, one pass), then dispatches the
+// T k <= 512 assignments and computes the balance statistics: three dependent
+// steps without a launch between them.  Each step's global results are read back
+// by the block after a barrier.
+template <int NB, int SPL>
+__global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
+    int T, int E, int k, int mode, int renorm, const float* __restrict__ sel_bias, const float* __restrict__ scores,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ near_tie, int64_t cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ perm_token, float alpha, float* __restrict__ f, float* __restrict__ P,
+    float* __restrict__ l_aux, float* __restrict__ max_over_mean) {
+  select_tile<NB, SPL, 1, false, 16>(scores, E, 0, T, E, k, mode, renorm, sel_bias, nullptr, topk_idx, topk_w,
+                                     near_tie);
+  __syncthreads();
+  dispatch_single(topk_idx, (int64_t)T * k, k, E, cap, 0, counts, offsets, row_of, perm_token);
+  __syncthreads();
+  stats_single(scores, T, E, counts, k, alpha, f, P, l_aux, max_over_mean);
+}
+
 template <int NB, int SPL>
 __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
@@ -650,6 +672,24 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int NB, int SPL>
+hipError_t launch_dispatch_small(const RouteDispatchArgs& d, hipStream_t stream) {
+  const RouteArgs& a = d.route;
+  const dim3 sgrid((a.T + kSplitTile - 1) / kSplitTile, (a.E + kSplitTile - 1) / kSplitTile);
+  hipLaunchKernelGGL(route_scores_split_kernel, sgrid, dim3(kSplitWaves * 64), 0, stream, (const uint16_t*)a.x,
+                     (const uint16_t*)a.w_router, a.bias, a.T, a.d, a.E, a.logits);
+  hipLaunchKernelGGL((route_dispatch_small_kernel<NB, SPL>), dim3(1), dim3(1024), 0, stream, a.T, a.E, a.k, a.mode,
+                     a.renorm, a.select_bias, a.logits, a.topk_idx, a.topk_w, a.near_tie, d.capacity, d.counts,
+                     d.offsets, d.row_of, d.perm_token, d.alpha, d.f, d.P, d.l_aux, d.max_over_mean);
+  return hipGetLastError();
+}
+
+template <int NB>
+hipError_t launch_dispatch_small_nb(const RouteDispatchArgs& d, hipStream_t stream) {
+  if (d.route.k <= 16) return launch_dispatch_small<NB, 1>(d, stream);
+  return launch_dispatch_small<NB, NB>(d, stream);
+}
+
 template <int NB>
 hipError_t launch_nb(const RouteArgs& a, hipStream_t stream) {
   // slots per lane: one when k <= 16, else NB (k <= E <= 16 NB)
@@ -658,6 +698,20 @@ hipError_t launch_nb(const RouteArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool route_dispatch_small_fits(int dtype, int T, int k, int E) {
+  return dtype == MOE_BF16 && T >= 1 && T <= kSingleStatsTokens && (int64_t)T * k <= kSingleMaxPairs &&
+         T <= MOE_ROUTE_SPLIT_MAX_T && E >= 1 && E <= MOE_MAX_EXPERTS;
+}
+
+hipError_t launch_route_dispatch_small(const RouteDispatchArgs& d, hipStream_t stream) {
+  const int E = d.route.E;
+  if (E <= 16) return launch_dispatch_small_nb<1>(d, stream);
+  if (E <= 32) return launch_dispatch_small_nb<2>(d, stream);
+  if (E <= 64) return launch_dispatch_small_nb<4>(d, stream);
+  if (E <= 128) return launch_dispatch_small_nb<8>(d, stream);
+  return launch_dispatch_small_nb<16>(d, stream);
+}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (a.E <= 16) return launch_nb<1>(a, stream);

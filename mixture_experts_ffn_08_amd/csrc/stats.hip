@@ -12,6 +12,7 @@
 // does everything in one launch.  No atomics: results are deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "stats_single.h"
 
 namespace moe {
 namespace {
@@ -114,77 +115,14 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   }
 }
 
-// All T <= 64 tokens in one block of 16 waves: each 16-lane row takes one token
-// (lane r holds experts r + 16 i), its softmax goes to LDS, and thread e sums
-// column e over the tokens in token order.  f, P, L_aux and max/mean as in
-// finish_stats, with the two block-wide reductions done by wave shuffles (fixed
-// tree) and one LDS step.
+// All T <= 64 tokens in one block of 16 waves (stats_single).
+static_assert(kStatsTokens == kSingleStatsTokens, "one block takes T <= kStatsTokens");
 __global__ __launch_bounds__(1024) void stats_small_kernel(const float* __restrict__ logits, int T, int E,
                                                             const int32_t* __restrict__ counts, int k, float alpha,
                                                             float* __restrict__ f, float* __restrict__ P,
                                                             float* __restrict__ l_aux,
                                                             float* __restrict__ max_over_mean) {
-  constexpr int NB = MOE_MAX_EXPERTS / 16;
-  constexpr int S = MOE_MAX_EXPERTS + 1;  // LDS row stride (floats)
-  __shared__ float prob[kStatsTokens * S];
-  __shared__ double w_fp[16];
-  __shared__ int w_max[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, t = wave * 4 + (lane >> 4);
-  const bool live = t < T;
-  const float* row = logits + (size_t)min(t, T - 1) * E;
-  float v[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) v[i] = row[min(r + 16 * i, E - 1)];  // all loads first, clamped
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (r + 16 * i < E) m = fmaxf(m, v[i]);
-  m = row16_max(m);
-  float z = 0.f;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    v[i] = r + 16 * i < E ? __expf(v[i] - m) : 0.f;
-    z += v[i];
-  }
-  const float inv = 1.f / row16_sum(z);
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (r + 16 * i < E) prob[t * S + r + 16 * i] = live ? v[i] * inv : 0.f;
-  __syncthreads();
-  const float tk = (float)((int64_t)T * k);
-  double fp = 0.0;
-  int c = 0;
-  if (tid < E) {
-    float acc = 0.f;
-    for (int u = 0; u < T; ++u) acc += prob[u * S + tid];
-    const float p = (float)((double)acc / (double)T);
-    c = counts[tid];
-    const float fi = (float)c / tk;
-    f[tid] = fi;
-    P[tid] = p;
-    fp = (double)fi * (double)p;
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    fp += __shfl_xor(fp, o, 64);
-    c = max(c, __shfl_xor(c, o, 64));
-  }
-  if (lane == 0) {
-    w_fp[wave] = fp;
-    w_max[wave] = c;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    double sum = 0.0;
-    int cmax = 0;
-    for (int w = 0; w < 16; ++w) {
-      sum += w_fp[w];
-      cmax = max(cmax, w_max[w]);
-    }
-    *l_aux = (float)((double)alpha * (double)E * sum);
-    *max_over_mean = (float)((int64_t)E * cmax) / tk;
-  }
+  stats_single(logits, T, E, counts, k, alpha, f, P, l_aux, max_over_mean);
 }
 
 // One block.  Thread (g, e) sums partial[b][e] over blocks b = g, g + G, ... in

@@ -96,6 +96,8 @@ class Buffers:
                                        dtype=torch.uint8, device=dev) if scatter else None)
         # ordering between the main stream and a side stream running the statistics
         self.fork_event, self.stats_event = torch.cuda.Event(), torch.cuda.Event()
+        # moe_layer_args structs of this buffer set, by layer and input
+        self.layer_args = {}
         if s.F_shared > 0:
             self.shared_offsets = torch.tensor([0, T], dtype=i32, device=dev)
             self.shared_a = torch.empty((max(T, 1), s.F_shared), dtype=td, device=dev)
@@ -216,6 +218,18 @@ class MoeLayer:
             return b
         s = self.shape
         st = stream if stream is not None else torch.cuda.current_stream()
+        if b.ws_scatter is None and b.x_perm is None:
+            # the whole layer in one library call (the fused decode form inside it);
+            # the materialized gather and the scatter combine take the separate calls
+            key = (id(self.w), s, x.data_ptr(), tuple(x.shape), x.dtype)
+            args = b.layer_args.get(key)
+            if args is None:
+                cap = _lib.moe_capacity(b.T, s.k, s.E, s.phi)
+                args = b.layer_args[key] = _lib.layer_args(s, x, self.w, b, cap)
+            side = side_stream if side_stream is not None and b.T * s.k > SMALL_GROUP_ROWS * s.E else None
+            _lib.moe_layer_forward(args, st, side, b.fork_event if side else None, b.stats_event if side else None,
+                                   marks)
+            return b
         self.route(x, b, st)
         self.permute(x, b, st)
         if side_stream is not None and b.T * s.k <= SMALL_GROUP_ROWS * s.E:

@@ -217,3 +217,55 @@ def test_down_combine_rejects_before_launch():
     assert call(G=0) == _lib.MOE_ERR_INVALID_ARG
     assert call(dt=7) == _lib.MOE_ERR_INVALID_ARG
     assert call(T=0, a=None, off=None, w=None, pt=None, ro=None, tw=None, y=None, ws=None, wsb=0) == _lib.MOE_OK
+
+
+def test_layer_args_struct_matches_the_header():
+    assert _lib.load().moe_layer_args_size() == ctypes.sizeof(_lib.MoeLayerArgs)
+
+
+def test_layer_forward_rejects_before_launch():
+    """moe_layer_forward runs every call's checks before it enqueues anything: a bad
+    argument of any step returns that step's status and message, and nothing runs."""
+    lib = _lib.load()
+    assert lib.moe_layer_forward(None, None) == _lib.MOE_ERR_INVALID_ARG
+    T, d, E, k, F = 16, 128, 8, 2, 256
+    a = _lib.MoeLayerArgs()
+    a.dtype, a.T, a.d, a.E, a.k, a.F, a.F_shared = _lib.MOE_BF16, T, d, E, k, F, 0
+    a.mode, a.renorm, a.capacity, a.alpha = 0, 1, -1, 0.01
+    for name, _ in _lib.MoeLayerArgs._fields_:
+        if name not in ("dtype", "T", "d", "E", "k", "F", "F_shared", "mode", "renorm", "capacity", "alpha",
+                        "logit_bias", "select_bias", "shared_gate", "shared_up", "shared_down", "shared_offsets",
+                        "shared_a", "shared_y", "side_stream", "fork_event", "join_event", "marks",
+                        "permute_workspace_bytes", "stats_workspace_bytes"):
+            setattr(a, name, 0x1000)
+    a.permute_workspace_bytes = _lib.moe_permute_workspace_bytes(T, k, E)
+    a.stats_workspace_bytes = 1 << 20
+
+    def call(**kw):
+        b = _lib.MoeLayerArgs.from_buffer_copy(a)
+        for key, v in kw.items():
+            setattr(b, key, v)
+        return lib.moe_layer_forward(ctypes.byref(b), None), _lib.last_error()
+
+    st, msg = call(E=0)
+    assert st == _lib.MOE_ERR_INVALID_ARG and msg.startswith("moe_route")
+    st, msg = call(mode=9)
+    assert st == _lib.MOE_ERR_INVALID_ARG and msg.startswith("moe_route")
+    st, msg = call(permute_workspace_bytes=4)
+    assert st == _lib.MOE_ERR_WORKSPACE and msg.startswith("moe_permute")
+    st, msg = call(F=100)
+    assert st == _lib.MOE_ERR_UNSUPPORTED and msg.startswith("moe_grouped_gate_up")
+    st, msg = call(y_perm=None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and msg.startswith("moe_grouped_down")
+    st, msg = call(y=None)
+    assert st == _lib.MOE_ERR_INVALID_ARG and msg.startswith("moe_combine")
+    st, msg = call(stats_workspace_bytes=0)
+    assert st == _lib.MOE_ERR_WORKSPACE and msg.startswith("moe_stats")
+    st, msg = call(F_shared=256)
+    assert st == _lib.MOE_ERR_INVALID_ARG and "shared_offsets" in msg
+    st, msg = call(F_shared=256, shared_offsets=0x1000)
+    assert st == _lib.MOE_ERR_INVALID_ARG and msg.startswith("moe_grouped")
+    st, msg = call(T=-1)
+    assert st == _lib.MOE_ERR_INVALID_ARG
+    st, _ = call(T=0)
+    assert st == _lib.MOE_OK
