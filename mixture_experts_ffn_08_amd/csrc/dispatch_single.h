@@ -17,9 +17,13 @@ constexpr int kSingleMaxPairs = 512;             // assignments one block dispat
 constexpr int kSingleWords = kSingleMaxPairs / 32;  // bitmap words per expert
 
 // Called by every thread of a block of at least kSingleMaxPairs threads; P <= 512.
+// idx may be in LDS.  The block's threads exchange data through LDS only, so the
+// barriers wait for LDS operations, not for global stores.  counts_copy (LDS or
+// global, may be NULL) receives the counts as well.
 __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t P, int k, int E, int64_t cap,
                                        int padded, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                       int32_t* __restrict__ row_of, int32_t* __restrict__ perm_token) {
+                                       int32_t* __restrict__ row_of, int32_t* __restrict__ perm_token,
+                                       int32_t* __restrict__ counts_copy = nullptr) {
   __shared__ uint32_t mask[MOE_MAX_EXPERTS * kSingleWords];
   __shared__ int cnt[MOE_MAX_EXPERTS];
   __shared__ int kept[MOE_MAX_EXPERTS];
@@ -27,7 +31,7 @@ __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t 
   const int tid = threadIdx.x, nthr = blockDim.x;
   for (int i = tid; i < E * kSingleWords; i += nthr) mask[i] = 0u;
   for (int i = tid; i < E; i += nthr) cnt[i] = 0;
-  __syncthreads();
+  lds_barrier();
   const int e = tid < P ? idx[tid] : -1;
   const bool valid = (unsigned)e < (unsigned)E;
   const int w = tid >> 5;
@@ -36,18 +40,19 @@ __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t 
     atomicOr(&mask[e * kSingleWords + w], bit);
     atomicAdd(&cnt[e], 1);
   }
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < E; i += nthr) {
     counts[i] = cnt[i];
+    if (counts_copy != nullptr) counts_copy[i] = cnt[i];
     kept[i] = cap < 0 ? cnt[i] : (int)min((int64_t)cnt[i], cap);
     incl[0][i] = kept[i];
   }
-  __syncthreads();
+  lds_barrier();
   // inclusive scan of the kept counts over experts (Hillis-Steele, ping-pong buffers)
   int src = 0;
   for (int h = 1; h < E; h <<= 1) {
     for (int i = tid; i < E; i += nthr) incl[src ^ 1][i] = incl[src][i] + (i >= h ? incl[src][i - h] : 0);
-    __syncthreads();
+    lds_barrier();
     src ^= 1;
   }
   if (!padded) {

@@ -108,7 +108,7 @@ template <int NB, int SPL, int PASSES, bool WRITE_SCORES, int NW = 4>
 __device__ void select_tile(const float* tile, int stride, int t0, int T, int E, int k, int mode, int renorm,
                             const float* __restrict__ sel_bias, float* __restrict__ logits,
                             int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                            int32_t* __restrict__ near_tie) {
+                            int32_t* __restrict__ near_tie, int32_t* __restrict__ idx_copy = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, row = lane >> 4;
   const bool biased = sel_bias != nullptr;
@@ -220,6 +220,7 @@ __device__ void select_tile(const float* tile, int stride, int t0, int T, int E,
         if (j < k) {
           topk_idx[(size_t)t * k + j] = (int32_t)my_idx[q];
           topk_w[(size_t)t * k + j] = base[q] * rden;
+          if (idx_copy != nullptr) idx_copy[(t - t0) * k + j] = (int32_t)my_idx[q];
         }
       }
       if (r == 0)
@@ -586,8 +587,9 @@ __global__ __launch_bounds__(256) void route_select_kernel(int T, int E, int k, 
 // Few tokens: after route_scores_split_kernel, one block of 16 waves selects for
 // all T <= 64 tokens (one token per 16-lane row, one pass), then dispatches the
 // T k <= 512 assignments and computes the balance statistics: three dependent
-// steps without a launch between them.  Each step's global results are read back
-// by the block after a barrier.
+// steps without a launch between them.  The chosen experts and the counts pass
+// from step to step through LDS, and the statistics' score loads are issued
+// before the selection.
 template <int NB, int SPL>
 __global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
     int T, int E, int k, int mode, int renorm, const float* __restrict__ sel_bias, const float* __restrict__ scores,
@@ -595,12 +597,16 @@ __global__ __launch_bounds__(1024) void route_dispatch_small_kernel(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_of,
     int32_t* __restrict__ perm_token, float alpha, float* __restrict__ f, float* __restrict__ P,
     float* __restrict__ l_aux, float* __restrict__ max_over_mean) {
+  __shared__ int32_t s_idx[kSingleMaxPairs];
+  __shared__ int32_t s_counts[MOE_MAX_EXPERTS];
+  float sv[kSingleStatsRegs];
+  stats_single_load(scores, T, E, sv);  // in flight through the selection
   select_tile<NB, SPL, 1, false, 16>(scores, E, 0, T, E, k, mode, renorm, sel_bias, nullptr, topk_idx, topk_w,
-                                     near_tie);
-  __syncthreads();
-  dispatch_single(topk_idx, (int64_t)T * k, k, E, cap, 0, counts, offsets, row_of, perm_token);
-  __syncthreads();
-  stats_single(scores, T, E, counts, k, alpha, f, P, l_aux, max_over_mean);
+                                     near_tie, s_idx);
+  lds_barrier();
+  dispatch_single(s_idx, (int64_t)T * k, k, E, cap, 0, counts, offsets, row_of, perm_token, s_counts);
+  lds_barrier();
+  stats_single_finish(sv, T, E, s_counts, k, alpha, f, P, l_aux, max_over_mean);
 }
 
 template <int NB, int SPL>
