@@ -24,7 +24,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_FLOPS = 256 * 4096 * 2.4e9      # dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
+PEAK_CLOCK_GHZ = 2.4
+PEAK_BF16_FLOPS = 256 * 4096 * PEAK_CLOCK_GHZ * 1e9  # dense bf16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM_BYTES = 8.0e12                   # HBM3E
 # The headline steps' untimed warm-up runs at least this long (W steps, then more
 # if W steps take less): the clock settles under load in tens of milliseconds.
@@ -86,6 +87,27 @@ def recorded_traffic():
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def recorded_clocks():
+    """Sustained clocks (GHz) of the gate/up and down launches from the counter
+    summary, or None if there is none or the kernel sources changed since."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "grouped_gemm_qwen3_prefill_mfma_l2.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, _, val = line.partition("=")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return float(fields["gate_up_clock_ghz"]), float(fields["down_clock_ghz"])
     except (KeyError, ValueError):
         return None
 
@@ -493,6 +515,15 @@ def main():
                          "frac_of_mfma_peak": (flops_gu + flops_dn) / ((gu_ms + dn_ms) * 1e-3) / PEAK_BF16_FLOPS,
                          "down_ms": dn_ms},
     }
+    clocks = recorded_clocks()
+    if clocks is not None:
+        # the MFMA peak at the clock the part sustains under this launch (from the counters)
+        peak_gu = PEAK_BF16_FLOPS * clocks[0] / PEAK_CLOCK_GHZ
+        peak_dn = PEAK_BF16_FLOPS * clocks[1] / PEAK_CLOCK_GHZ
+        result["roofline"]["clock_ghz"] = clocks[0]
+        result["roofline"]["frac_at_clock"] = achieved / peak_gu
+        result["grouped_gemm"]["down_clock_ghz"] = clocks[1]
+        result["grouped_gemm"]["down_frac_at_clock"] = flops_dn / (dn_ms * 1e-3) / peak_dn
     result.update(extra)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
