@@ -400,26 +400,34 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(
 //    keeps more CUs busy when T is small.
 //  * Each K step of 64 loads the block's x rows and E router rows (128 bytes
 //    each: whole lines) straight into LDS (buffer_load_dwordx4 ... lds writes
-//    lane l's 16 bytes at M0 + 16 l), three stages deep; each stage is its own
+//    lane l's 16 bytes at M0 + 16 l), four stages deep with 64 tokens (three with
+//    32); each stage is its own
 //    __shared__ array, so the compiler waits only for the DMA a read needs.
 //    16-byte chunk c of LDS row r sits at position c ^ ((r & 7) ^ ((r >> 3) & 1)):
 //    conflict-free fragment reads.
 //  * Measured (qwen3 shape, router alone, x in cache): T = 16384 24.3 us with 64
 //    tokens, 26.8 with 32, 35.9 for the register-operand scores and the separate
 //    selection; T = 4096 18.9 / 20.2; T = 2304 18.4 / 16.8 (36 against 72 busy CUs).
-//    A six-deep x ring beside a three-deep router ring ran slower (31.4 us).
-constexpr int kGemmStages = 3;
+//    Four stages against three with 64 tokens: 24.9 -> 23.6 us with x in cache,
+//    47.2 -> 44.7 us with x and W_r evicted first (a 512 MB write before each call);
+//    five: no further gain.  A six-deep x ring beside a three-deep router ring
+//    ran slower (31.4 us).
 constexpr int kGemmWideMinT = 4096;  // 64-token blocks from this T on
+// DMA stages of the 64-token form (the 32-token form, two blocks per CU, has three).
+#ifndef MOE_ROUTE_GEMM_WIDE_STAGES
+#define MOE_ROUTE_GEMM_WIDE_STAGES 4
+#endif
 __device__ __forceinline__ int route_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 typedef __attribute__((address_space(3))) void* route_lds_t;
 
-template <int SPL, int NW>
+template <int SPL, int NW, int STG>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ near_tie) {
   static_assert(NW == 4 || NW == 8, "32 or 64 tokens a block");
+  static_assert(STG == 3 || STG == 4, "DMA stages");
   constexpr int EP = 128, BK = 64, TT = 8 * NW;
   constexpr int RPW = 16 / NW;           // router DMA instructions per wave and step
   constexpr int STAGE = (TT + EP) * BK;  // bf16: TT x rows, then 128 router rows
@@ -427,6 +435,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t s0[STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s1[STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t s2[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t s3[STG > 3 ? STAGE : 8];
   __shared__ __attribute__((aligned(16))) float tile[TT * TSTR];
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
   const int t0 = blockIdx.x * TT;
   const int rows = min(TT, T - t0);
   const int nst = d / BK;
-  const int nsteps = (nst + kGemmStages - 1) / kGemmStages * kGemmStages;  // padded with zero steps
+  const int nsteps = (nst + STG - 1) / STG * STG;  // padded with zero steps
   // over the block's token rows only (32-bit offsets whatever T is)
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (size_t)t0 * d), (short)0, (int)((uint32_t)rows * (uint32_t)d * 2u), kBufferFlags);
@@ -486,19 +495,29 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
   };
   // Step s in stage `cur`: this wave's DMA of the stage has landed (the compiler
   // waits for it before the read below), then every wave's has and every wave
-  // has finished the previous stage, which takes the DMA of step s + 2.
+  // has finished the previous stage, which takes the DMA of step s + STG - 1.
   auto step = [&](uint16_t* cur, uint16_t* prev, int s) __attribute__((always_inline)) {
     const uint32_t probe = *reinterpret_cast<const uint32_t*>(cur + lane * 2);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"v"(probe) : "memory");
-    dma(prev, s + kGemmStages - 1);
+    dma(prev, s + STG - 1);
     compute(cur);
   };
   dma(s0, 0);
   dma(s1, 1);
-  for (int s = 0; s < nsteps; s += kGemmStages) {
-    step(s0, s2, s);
-    step(s1, s0, s + 1);
-    step(s2, s1, s + 2);
+  if constexpr (STG == 3) {
+    for (int s = 0; s < nsteps; s += 3) {
+      step(s0, s2, s);
+      step(s1, s0, s + 1);
+      step(s2, s1, s + 2);
+    }
+  } else {
+    dma(s2, 2);
+    for (int s = 0; s < nsteps; s += 4) {
+      step(s0, s3, s);
+      step(s1, s0, s + 1);
+      step(s2, s1, s + 2);
+      step(s3, s2, s + 3);
+    }
   }
   // the padding DMAs (zeros, past the last step) land before the block ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -649,11 +668,11 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
   } else if (a.dtype == MOE_BF16 && NB == 8 && MOE_ROUTE_GEMM) {
     // 64 < E <= 128: scores as a DMA-fed GEMM, selection in the same block
     if (a.T >= kGemmWideMinT)
-      hipLaunchKernelGGL((route_gemm_kernel<SPL, 8>), dim3((a.T + 63) / 64), dim3(512), 0, stream,
+      hipLaunchKernelGGL((route_gemm_kernel<SPL, 8, MOE_ROUTE_GEMM_WIDE_STAGES>), dim3((a.T + 63) / 64), dim3(512), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
                          a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
     else
-      hipLaunchKernelGGL((route_gemm_kernel<SPL, 4>), dim3((a.T + 31) / 32), dim3(256), 0, stream,
+      hipLaunchKernelGGL((route_gemm_kernel<SPL, 4, 3>), dim3((a.T + 31) / 32), dim3(256), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
                          a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
   } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
