@@ -303,7 +303,8 @@ def ep_share(weights, x, bufs, shape, stream, torch, gpus: int = 8, phi: float =
 def config_sweep(steps: int, warmup: int):
     """Time the layer on every configured shape (synthetic inputs, seed 0): one
     JSON line each with tokens/s, the routed and shared expert FLOPs against the
-    bf16 MFMA peak, and the algorithmic bytes against HBM."""
+    bf16 MFMA peak, the algorithmic bytes against HBM, and (prefill shapes) one
+    GPU's share of the layer under 8-way expert parallelism."""
     import torch
 
     from mixture_experts_ffn_08_amd import inputs as minp
@@ -325,6 +326,9 @@ def config_sweep(steps: int, warmup: int):
         R = int(bufs.offsets[-1].item())
         touched = int((bufs.counts > 0).sum().item())
         s = shape
+        # one GPU's share under 8-way expert parallelism, on this layer's own routing
+        with torch.cuda.stream(stream):
+            eps = ep_share(weights, x, bufs, shape, stream, torch) if s.T >= 1024 and s.E >= 8 else None
         routed_flops = 6.0 * R * s.d * s.F
         shared_flops = 6.0 * s.T * s.d * s.F_shared
         flops = routed_flops + shared_flops + 2.0 * s.T * s.d * s.E
@@ -341,7 +345,7 @@ def config_sweep(steps: int, warmup: int):
             "max_over_mean": float(bufs.max_over_mean.item()),
             "layer_tflops": flops / (ms * 1e-3) / 1e12, "frac_of_mfma_peak": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
             "algorithmic_bytes": nbytes, "hbm_frac": nbytes / (ms * 1e-3) / PEAK_HBM_BYTES,
-            "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1)}), flush=True)
+            "ep_share": eps, "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1)}), flush=True)
         del weights, layer, x, bufs, inp
         torch.cuda.empty_cache()
 

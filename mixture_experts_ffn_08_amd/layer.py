@@ -58,6 +58,11 @@ class DeviceWeights:
         self.shared = None if sh is None else tuple(to_device(m, s.dtype, self.device) for m in sh)
         torch.cuda.synchronize(self.device)
 
+    def addresses(self) -> tuple:
+        """Device addresses of every weight tensor (0 for an absent one)."""
+        ts = (self.w_router, self.bias, self.select_bias, self.gate, self.up, self.down) + (self.shared or (None,) * 3)
+        return tuple(0 if t is None else t.data_ptr() for t in ts)
+
 
 class Buffers:
     """Every intermediate and output of the layer for T tokens (device memory).
@@ -96,8 +101,8 @@ class Buffers:
                                        dtype=torch.uint8, device=dev) if scatter else None)
         # ordering between the main stream and a side stream running the statistics
         self.fork_event, self.stats_event = torch.cuda.Event(), torch.cuda.Event()
-        # moe_layer_args structs of this buffer set, by layer and input
-        self.layer_args = {}
+        # (key, moe_layer_args) of the last one-call forward on this buffer set
+        self.layer_args = None
         if s.F_shared > 0:
             self.shared_offsets = torch.tensor([0, T], dtype=i32, device=dev)
             self.shared_a = torch.empty((max(T, 1), s.F_shared), dtype=td, device=dev)
@@ -221,11 +226,13 @@ class MoeLayer:
         if b.ws_scatter is None and b.x_perm is None:
             # the whole layer in one library call (the fused decode form inside it);
             # the materialized gather and the scatter combine take the separate calls
-            key = (id(self.w), s, x.data_ptr(), tuple(x.shape), x.dtype)
-            args = b.layer_args.get(key)
-            if args is None:
+            # the struct holds device addresses only: reuse it while every address and
+            # the shape are the same (a new tensor at a reused address is then as valid)
+            key = (s, tuple(x.shape), x.dtype, x.data_ptr()) + self.w.addresses()
+            if b.layer_args is None or b.layer_args[0] != key:
                 cap = _lib.moe_capacity(b.T, s.k, s.E, s.phi)
-                args = b.layer_args[key] = _lib.layer_args(s, x, self.w, b, cap)
+                b.layer_args = (key, _lib.layer_args(s, x, self.w, b, cap))
+            args = b.layer_args[1]
             side = side_stream if side_stream is not None and b.T * s.k > SMALL_GROUP_ROWS * s.E else None
             _lib.moe_layer_forward(args, st, side, b.fork_event if side else None, b.stats_event if side else None,
                                    marks)
