@@ -21,7 +21,16 @@ from support import TOL, ExpertCache, LayerRun, assert_same_sum, check_dispatch,
 
 pytestmark = pytest.mark.gpu
 
-CONFIGS = ["tiny_f32", "mixtral", "mixtral_cap", "qwen2", "qwen3_prefill", "qwen3_decode", "dsv3_skew"]
+CONFIGS = ["tiny_f32", "mixtral", "mixtral_cap", "qwen2", "qwen3_prefill", "qwen3_decode", "dsv3_skew",
+           # dropping at full size: the configured phi = 1.25 drops nothing at seed 0, these do
+           "mixtral_phi1.0", "mixtral_phi0.5", "tiny_f32_phi1.25"]
+
+
+def config_shape(name):
+    """A configured shape, or one with another capacity factor ("<shape>_phi<phi>")."""
+    base, _, phi = name.partition("_phi")
+    s = minp.SHAPES[base]
+    return s if not phi else s.with_(phi=float(phi), name=name)
 
 
 def weights_by_expert(idx_gpu, idx_ref, w_ref, ok):
@@ -43,7 +52,7 @@ def rowwise_rel(gpu, ref):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", CONFIGS)
 def test_config_parity(name):
-    shape = minp.SHAPES[name]
+    shape = config_shape(name)
     s = shape
     t0 = time.time()
     inp = minp.LayerInputs(shape, seed=0)
@@ -67,6 +76,8 @@ def test_config_parity(name):
             if not tie.any():
                 assert dropped_gpu == dropped_ref
             log(f"[{name}] capacity {cap}: {len(dropped_gpu)} dropped assignments (oracle routing: {len(dropped_ref)})")
+            if "_phi" in name:
+                assert len(dropped_gpu) > 0, "this capacity factor must drop assignments"
         xs = minp.as_f32(inp.x, s.dtype)
         ex = ExpertCache(inp)
         tol = TOL[s.dtype]
