@@ -14,6 +14,8 @@
 //   scan_kernel   one block: per-expert scan over blocks, demand counts,
 //                 capacity, exclusive scan over experts -> offsets
 //   rank_kernel   bitmap ranks -> row_of, perm_token
+//   rank_scan_kernel        scan + rank in one launch, up to 256 blocks: each block
+//                           sums the histograms it needs itself
 //   permute_single_kernel   the three above in one block when T k <= 512
 //   gather_kernel x_perm[r] = x[perm_token[r]], one wave per row, 16-byte lanes
 #include <algorithm>
@@ -25,6 +27,9 @@
 namespace moe {
 namespace {
 
+#ifndef MOE_RANK_SCAN
+#define MOE_RANK_SCAN 1
+#endif
 constexpr int kBP = kPairsPerBlock;  // 512 threads, one assignment each
 constexpr int kWords = kBP / 32;     // bitmap words per expert
 
@@ -150,6 +155,94 @@ __global__ __launch_bounds__(kBP) void rank_kernel(const int32_t* __restrict__ i
   row_of[p] = row;
 }
 
+// rank_kernel with the scan folded in, for up to kRankScanMaxBlocks blocks: each
+// block sums the per-block histograms itself (its base, the assignments of earlier
+// blocks, and the totals), scans the kept totals over experts for the offsets, then
+// ranks as rank_kernel does; block 0 writes counts and offsets.  Integer sums, so
+// the results are those of scan_kernel + rank_kernel whatever the order.  Every
+// block reads all nblk x E counts (L2), which is why the block count is bounded.
+constexpr int kRankScanMaxBlocks = 256;
+
+__global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restrict__ idx, int64_t P, int k, int E,
+                                                         int64_t cap, int padded,
+                                                         const int32_t* __restrict__ block_counts, int nblk, int ep,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ row_of,
+                                                         int32_t* __restrict__ perm_token) {
+  __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
+  __shared__ int part_base[kBP], part_total[kBP];
+  __shared__ int base_s[MOE_MAX_EXPERTS], kept_s[MOE_MAX_EXPERTS], incl[2][MOE_MAX_EXPERTS];
+  constexpr int kBatch = 16;  // loads in flight per thread
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kBP) mask[i] = 0u;
+  // Sums over the blocks: thread (c, e) = (tid / ep, tid % ep) (ep >= E a power of
+  // two) takes chunk c of the block list; expert fastest, so a wave reads runs of
+  // consecutive experts' counts.  Clamped loads, out-of-range terms zeroed.
+  const int e2 = tid % ep, c = tid / ep, nch = kBP / ep;
+  const int chunk = (nblk + nch - 1) / nch;
+  const int b0 = min(c * chunk, nblk), b1 = e2 < E ? min(b0 + chunk, nblk) : b0;
+  const int ec = e2 < E ? e2 : 0;
+  const int me = blockIdx.x;
+  int sb = 0, st = 0;
+  for (int b = b0; b < b1; b += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) v[q] = block_counts[(size_t)min(b + q, b1 - 1) * E + ec];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int x = b + q < b1 ? v[q] : 0;
+      st += x;
+      sb += b + q < me ? x : 0;
+    }
+  }
+  part_base[tid] = sb;
+  part_total[tid] = st;
+  __syncthreads();
+  const int64_t p = (int64_t)blockIdx.x * kBP + tid;
+  const int e = p < P ? idx[p] : -1;
+  const bool valid = (unsigned)e < (unsigned)E;
+  const int w = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid) atomicOr(&mask[e * kWords + w], bit);
+  if (tid < E) {
+    int base = 0, total = 0;
+    for (int q = 0; q < nch; ++q) {
+      base += part_base[q * ep + tid];
+      total += part_total[q * ep + tid];
+    }
+    base_s[tid] = base;
+    const int kept = cap < 0 ? total : (int)min((int64_t)total, cap);
+    kept_s[tid] = kept;
+    incl[0][tid] = kept;
+    if (me == 0) counts[tid] = total;
+  }
+  __syncthreads();
+  // inclusive scan of the kept totals over experts (Hillis-Steele, ping-pong buffers)
+  int src = 0;
+  for (int h = 1; h < E; h <<= 1) {
+    if (tid < E) incl[src ^ 1][tid] = incl[src][tid] + (tid >= h ? incl[src][tid - h] : 0);
+    __syncthreads();
+    src ^= 1;
+  }
+  if (me == 0 && !padded) {
+    if (tid < E) offsets[tid + 1] = incl[src][tid];
+    if (tid == 0) offsets[0] = 0;
+  }
+  if (p >= P) return;
+  int32_t row = -1;
+  if (valid) {
+    const uint32_t* m = mask + e * kWords;
+    int r = __popc(m[w] & (bit - 1u));
+    for (int q = 0; q < w; ++q) r += __popc(m[q]);
+    const int rank = base_s[e] + r;
+    if (cap < 0 || rank < cap) {
+      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept_s[e] + rank;
+      perm_token[row] = (int32_t)(p / k);
+    }
+  }
+  row_of[p] = row;
+}
+
 __global__ __launch_bounds__(256) void gather_kernel(const char* __restrict__ x,
                                                       const int32_t* __restrict__ perm_token,
                                                       const int32_t* __restrict__ offsets_end, int T,
@@ -207,6 +300,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   if (nblk == 1) {
     hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
                        a.padded, a.counts, a.offsets, a.row_of, a.perm_token);
+  } else if (nblk <= kRankScanMaxBlocks && MOE_RANK_SCAN) {
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
+    hipLaunchKernelGGL(rank_scan_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
+                       a.padded, a.block_counts, nblk, ep, a.counts, a.offsets, a.row_of, a.perm_token);
   } else {
     hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, ep, tpe,
