@@ -460,11 +460,26 @@ int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
     if (check || L.marks[i] == nullptr) return MOE_OK;
     return hip_status(hipEventRecord(L.marks[i], stream), "moe_layer_forward");
   };
-  if (check || !fused) {
+  // The router's blocks can write the dispatch's per-block histograms (into the
+  // permute workspace), which then skips its histogram launch.
+  const bool hist = moe::route_writes_block_hist(L.dtype, L.T, L.E, L.k);
+  if (check || (!fused && !hist)) {
     CHECK(moe_route(L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode, L.renorm,
                     L.logits, L.topk_idx, L.topk_w, L.near_tie, stream));
     CHECK(moe_permute(L.topk_idx, L.T, L.k, L.E, L.capacity, L.x, L.dtype, L.d, L.counts, L.offsets, L.row_of,
                       L.perm_token, nullptr, L.permute_workspace, L.permute_workspace_bytes, stream));
+  }
+  if (!check && !fused && hist) {
+    // the two calls above, their checks passed, with the histogram handed over
+    int32_t* block_counts = static_cast<int32_t*>(L.permute_workspace);
+    int32_t* block_base = reinterpret_cast<int32_t*>(static_cast<char*>(L.permute_workspace) +
+                                                     moe_permute_workspace_bytes(L.T, L.k, L.E) / 2);
+    moe::RouteArgs r{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,
+                     L.renorm ? 1 : 0, L.logits, L.topk_idx, L.topk_w, L.near_tie, block_counts};
+    CHECK(hip_status(moe::launch_route(r, stream), "moe_layer_forward"));
+    moe::PermuteArgs pa{L.topk_idx, L.T, L.k, L.E, L.capacity < 0 ? -1 : L.capacity, L.x, L.d * elem_bytes(L.dtype),
+                        L.counts, L.offsets, L.row_of, L.perm_token, nullptr, block_counts, block_base, 0, 1};
+    CHECK(hip_status(moe::launch_permute(pa, stream), "moe_layer_forward"));
   }
   if (!check && fused) {
     moe::RouteDispatchArgs a{{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,

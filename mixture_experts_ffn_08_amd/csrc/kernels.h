@@ -20,6 +20,9 @@ struct RouteArgs {
   int32_t* topk_idx;
   float* topk_w;
   int32_t* near_tie;
+  // [nblk][E] or null: with route_writes_block_hist, the histogram of each block of
+  // kPairsPerBlock assignments (the dispatch's hist_kernel output) is written too
+  int32_t* block_hist = nullptr;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
@@ -59,8 +62,12 @@ struct PermuteArgs {
   int32_t* block_counts;  // workspace [nblk][E]
   int32_t* block_base;    // workspace [nblk][E]
   int padded;             // 1: slot e * capacity + rank, offsets e * capacity, padding -1 / zero rows
+  int hist_given = 0;     // 1: block_counts already hold the per-block histograms (the router wrote them)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// Whether launch_route with a block_hist writes the dispatch's per-block histograms
+// for these sizes (its blocks of 64 tokens then hold exactly kPairsPerBlock assignments).
+bool route_writes_block_hist(int dtype, int T, int E, int k);
 
 struct GroupedGemmArgs {
   const void* A;        // [max_rows][K], or [a_nrows][K] read through a_rows

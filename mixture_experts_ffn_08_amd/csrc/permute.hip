@@ -301,11 +301,13 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(permute_single_kernel, dim3(1), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
                        a.padded, a.counts, a.offsets, a.row_of, a.perm_token);
   } else if (nblk <= kRankScanMaxBlocks && MOE_RANK_SCAN) {
-    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
+    if (!a.hist_given)
+      hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
     hipLaunchKernelGGL(rank_scan_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
                        a.padded, a.block_counts, nblk, ep, a.counts, a.offsets, a.row_of, a.perm_token);
   } else {
-    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
+    if (!a.hist_given)
+      hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, stream, a.block_counts, nblk, a.E, ep, tpe,
                        a.capacity, a.padded, a.block_base, a.counts, a.offsets);
     hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,

@@ -435,7 +435,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ near_tie) {
+    int32_t* __restrict__ near_tie, int32_t* __restrict__ block_hist) {
   static_assert(NW == 4 || NW == 8, "32 or 64 tokens a block");
   static_assert(STG == 3 || STG == 4, "DMA stages");
   constexpr int EP = 128, BK = 64, TT = 8 * NW;
@@ -562,8 +562,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
     tile[(32 * th + frow) * TSTR + n] = acc[e] + b;
   }
   __syncthreads();
+  // With block_hist (k = 8, so the block's TT k = 512 assignments are one dispatch
+  // block), the chosen experts also go to LDS and the block writes their histogram.
+  __shared__ int32_t s_idx[TT * 8];
+  __shared__ int32_t s_cnt[EP];
+  if (block_hist != nullptr && tid < EP) s_cnt[tid] = 0;
   select_tile<8, SPL, TT / (4 * NW), true, NW>(tile, TSTR, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx,
-                                                topk_w, near_tie);
+                                                topk_w, near_tie, block_hist != nullptr ? s_idx : nullptr);
+  if (block_hist == nullptr) return;  // uniform
+  __syncthreads();
+  for (int i = tid; i < rows * 8; i += 64 * NW) atomicAdd(&s_cnt[s_idx[i]], 1);
+  __syncthreads();
+  if (tid < E) block_hist[(size_t)blockIdx.x * E + tid] = s_cnt[tid];
 }
 
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
@@ -702,11 +712,12 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
     if (a.T >= kGemmWideMinT)
       hipLaunchKernelGGL((route_gemm_kernel<SPL, 8, MOE_ROUTE_GEMM_WIDE_STAGES>), dim3((a.T + 63) / 64), dim3(512), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
-                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
+                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie,
+                         route_writes_block_hist(a.dtype, a.T, a.E, a.k) ? a.block_hist : nullptr);
     else
       hipLaunchKernelGGL((route_gemm_kernel<SPL, 4, 3>), dim3((a.T + 31) / 32), dim3(256), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
-                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie);
+                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie, nullptr);
   } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
              (int64_t)a.T * ((a.E + kScoreSplitExperts - 1) / kScoreSplitExperts) <= kScoreSplitMaxRowReads) {
     // many experts: 64-expert score blocks (two per CU), then selection; each block
@@ -755,6 +766,11 @@ hipError_t launch_nb(const RouteArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool route_writes_block_hist(int dtype, int T, int E, int k) {
+  return dtype == MOE_BF16 && MOE_ROUTE_GEMM && T > MOE_ROUTE_SPLIT_MAX_T && T >= kGemmWideMinT && E > 64 &&
+         E <= 128 && k == 8 && 64 * k == kPairsPerBlock;
+}
 
 bool route_dispatch_small_fits(int dtype, int T, int k, int E) {
   return dtype == MOE_BF16 && T >= 1 && T <= kSingleStatsTokens && (int64_t)T * k <= kSingleMaxPairs &&

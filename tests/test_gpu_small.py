@@ -205,6 +205,9 @@ LAYER_CALL_CASES = [
     next(s for s in SMALL if s.name == "E256_few_tokens"),
     # just past the one-block limits, and the other forms
     S("decode_k9", "bf16", 64, 128, 32, 9, 128, 0, SM_TK, True, None, False),
+    # 64-token router blocks with k = 8: the router writes the dispatch's histograms (ragged last block)
+    S("prefill_E128_k8_router_hist", "bf16", 4133, 128, 128, 8, 128, 0, SM_TK, True, None, False),
+    S("prefill_E96_k8_capacity", "bf16", 4100, 128, 96, 8, 128, 0, SIG, False, 0.9, False, select_bias=0.02),
     next(s for s in SMALL if s.name == "small_shared"),
     next(s for s in SMALL if s.name == "tiny_f32"),
     next(s for s in SMALL if s.name == "k_over_64"),
