@@ -361,7 +361,10 @@ size_t moe_stats_workspace_bytes(int T, int E);
  * the first call that rejects it.
  * With bf16, T <= 64 and T k <= 512 (decode batches) the selection, the
  * dispatch and the statistics run as one block after the score kernel, with no
- * launch between them: the results are bit-identical to the separate calls.
+ * launch between them.  With bf16, 64 < E <= 128, k = 8 and T >= 4096 the
+ * router's blocks also write the dispatch's per-block histograms and the
+ * statistics' partial sums.  Either way the results are bit-identical to the
+ * separate calls.
  * Sources: the five steps as each call cites them; Transformers & Math 17.2
  * equation for the layer sum.
  *
@@ -406,10 +409,13 @@ typedef struct moe_layer_args {
   size_t permute_workspace_bytes;
   void* stats_workspace;        /* >= moe_stats_workspace_bytes(T, E) */
   size_t stats_workspace_bytes;
-  /* Optional: with side_stream, fork_event and join_event all given (and not
-   * the decode form above), the statistics run on side_stream after the work
-   * before the combine, and `stream` waits for them before the call returns
-   * its last operation.  The events are the caller's (hipEventCreate...). */
+  /* Optional: with side_stream, fork_event and join_event all given, the
+   * statistics run on side_stream after the work before the combine, and
+   * `stream` waits for them before the call returns its last operation.  Not in
+   * the decode form above, nor where the router computes the statistics' partial
+   * sums itself (bf16, 64 < E <= 128, k = 8, T >= 4096): there their final
+   * reduction runs on `stream` right after the dispatch.  The events are the
+   * caller's (hipEventCreate...). */
   hipStream_t side_stream;
   hipEvent_t fork_event;
   hipEvent_t join_event;

@@ -474,12 +474,17 @@ int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
     int32_t* block_counts = static_cast<int32_t*>(L.permute_workspace);
     int32_t* block_base = reinterpret_cast<int32_t*>(static_cast<char*>(L.permute_workspace) +
                                                      moe_permute_workspace_bytes(L.T, L.k, L.E) / 2);
+    float* stats_partial = static_cast<float*>(L.stats_workspace);
     moe::RouteArgs r{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,
-                     L.renorm ? 1 : 0, L.logits, L.topk_idx, L.topk_w, L.near_tie, block_counts};
+                     L.renorm ? 1 : 0, L.logits, L.topk_idx, L.topk_w, L.near_tie, block_counts, stats_partial};
     CHECK(hip_status(moe::launch_route(r, stream), "moe_layer_forward"));
     moe::PermuteArgs pa{L.topk_idx, L.T, L.k, L.E, L.capacity < 0 ? -1 : L.capacity, L.x, L.d * elem_bytes(L.dtype),
                         L.counts, L.offsets, L.row_of, L.perm_token, nullptr, block_counts, block_base, 0, 1};
     CHECK(hip_status(moe::launch_permute(pa, stream), "moe_layer_forward"));
+    // the router wrote the statistics' partial sums: their final reduction needs
+    // only the counts, so it runs here (one block) and no side stream is used
+    moe::StatsArgs sa{L.counts, L.logits, L.T, L.k, L.E, L.alpha, L.f, L.P, L.l_aux, L.max_over_mean, stats_partial};
+    CHECK(hip_status(moe::launch_stats_final(sa, stream), "moe_layer_forward"));
   }
   if (!check && fused) {
     moe::RouteDispatchArgs a{{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,
@@ -498,7 +503,8 @@ int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
     CHECK(moe_grouped_swiglu(L.x, nullptr, 0, L.shared_offsets, 1, L.T, L.d, L.F_shared, L.shared_gate,
                              L.shared_up, L.shared_down, L.dtype, L.shared_a, L.shared_y, stream));
   CHECK(mark(3));
-  const bool side = !fused && L.side_stream != nullptr && L.fork_event != nullptr && L.join_event != nullptr;
+  const bool side = !fused && !hist && L.side_stream != nullptr && L.fork_event != nullptr &&
+                    L.join_event != nullptr;
   auto stats = [&](hipStream_t st) {
     return moe_stats(L.counts, L.logits, L.T, L.k, L.E, L.alpha, L.f, L.P, L.l_aux, L.max_over_mean,
                      L.stats_workspace, L.stats_workspace_bytes, st);
@@ -512,7 +518,7 @@ int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
   CHECK(moe_combine(L.y_perm, (int)R, L.row_of, L.topk_w, L.F_shared > 0 ? L.shared_y : nullptr, L.dtype, L.T, L.k,
                     L.d, L.y, stream));
   if (side && !check) return hip_status(hipStreamWaitEvent(stream, L.join_event, 0), "moe_layer_forward");
-  if (check || !fused) CHECK(stats(stream));
+  if (check || (!fused && !hist)) CHECK(stats(stream));
   return ok();
 }
 

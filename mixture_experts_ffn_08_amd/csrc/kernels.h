@@ -23,6 +23,9 @@ struct RouteArgs {
   // [nblk][E] or null: with route_writes_block_hist, the histogram of each block of
   // kPairsPerBlock assignments (the dispatch's hist_kernel output) is written too
   int32_t* block_hist = nullptr;
+  // [stats_blocks(T)][E] or null: with route_writes_block_hist, the per-block partial
+  // sums of the balance statistic P (stats_partial_kernel's output) as well
+  float* stats_partial = nullptr;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
@@ -123,5 +126,7 @@ struct StatsArgs {
   float* partial;  // workspace [nblk][E]
 };
 hipError_t launch_stats(const StatsArgs& a, hipStream_t stream);
+// The final reduction alone, over stats_blocks(T) partial rows another kernel wrote.
+hipError_t launch_stats_final(const StatsArgs& a, hipStream_t stream);
 
 }  // namespace moe

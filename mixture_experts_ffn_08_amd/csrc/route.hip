@@ -36,6 +36,7 @@
 #include "common.h"
 #include "dispatch_single.h"
 #include "kernels.h"
+#include "stats_partial.h"
 #include "stats_single.h"
 
 namespace moe {
@@ -435,7 +436,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ sel_bias, int T, int d, int E, int k, int mode, int renorm,
     float* __restrict__ logits, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    int32_t* __restrict__ near_tie, int32_t* __restrict__ block_hist) {
+    int32_t* __restrict__ near_tie, int32_t* __restrict__ block_hist, float* __restrict__ stats_part) {
   static_assert(NW == 4 || NW == 8, "32 or 64 tokens a block");
   static_assert(STG == 3 || STG == 4, "DMA stages");
   constexpr int EP = 128, BK = 64, TT = 8 * NW;
@@ -564,16 +565,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void route_gemm_kernel(
   __syncthreads();
   // With block_hist (k = 8, so the block's TT k = 512 assignments are one dispatch
   // block), the chosen experts also go to LDS and the block writes their histogram.
+  // With stats_part (TT = 64 tokens, the statistics' block), the block also writes
+  // its partial sums of P from the score tile, with the statistics' own code.
   __shared__ int32_t s_idx[TT * 8];
   __shared__ int32_t s_cnt[EP];
+  __shared__ float s_smax[64], s_sinv[64], s_red[256];
   if (block_hist != nullptr && tid < EP) s_cnt[tid] = 0;
   select_tile<8, SPL, TT / (4 * NW), true, NW>(tile, TSTR, t0, T, E, k, mode, renorm, sel_bias, logits, topk_idx,
                                                 topk_w, near_tie, block_hist != nullptr ? s_idx : nullptr);
-  if (block_hist == nullptr) return;  // uniform
+  if (block_hist == nullptr && stats_part == nullptr) return;  // uniform
   __syncthreads();
-  for (int i = tid; i < rows * 8; i += 64 * NW) atomicAdd(&s_cnt[s_idx[i]], 1);
+  if (block_hist != nullptr)
+    for (int i = tid; i < rows * 8; i += 64 * NW) atomicAdd(&s_cnt[s_idx[i]], 1);
+  if (TT == 64 && stats_part != nullptr)  // uniform; the call holds barriers
+    block_softmax_sums<64 * NW>(tile, TSTR, rows, E, s_smax, s_sinv, s_red, stats_part + (size_t)blockIdx.x * E);
   __syncthreads();
-  if (tid < E) block_hist[(size_t)blockIdx.x * E + tid] = s_cnt[tid];
+  if (block_hist != nullptr && tid < E) block_hist[(size_t)blockIdx.x * E + tid] = s_cnt[tid];
 }
 
 // Scores for few tokens: block (i, j) computes tokens 16 i .. 16 i + 15 against
@@ -713,11 +720,12 @@ hipError_t launch_variant(const RouteArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((route_gemm_kernel<SPL, 8, MOE_ROUTE_GEMM_WIDE_STAGES>), dim3((a.T + 63) / 64), dim3(512), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
                          a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie,
-                         route_writes_block_hist(a.dtype, a.T, a.E, a.k) ? a.block_hist : nullptr);
+                         route_writes_block_hist(a.dtype, a.T, a.E, a.k) ? a.block_hist : nullptr,
+                         route_writes_block_hist(a.dtype, a.T, a.E, a.k) ? a.stats_partial : nullptr);
     else
       hipLaunchKernelGGL((route_gemm_kernel<SPL, 4, 3>), dim3((a.T + 31) / 32), dim3(256), 0, stream,
                          (const uint16_t*)a.x, (const uint16_t*)a.w_router, a.bias, a.select_bias, a.T, a.d, a.E,
-                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie, nullptr);
+                         a.k, a.mode, a.renorm, a.logits, a.topk_idx, a.topk_w, a.near_tie, nullptr, nullptr);
   } else if (a.dtype == MOE_BF16 && a.E > kScoreSplitExperts &&
              (int64_t)a.T * ((a.E + kScoreSplitExperts - 1) / kScoreSplitExperts) <= kScoreSplitMaxRowReads) {
     // many experts: 64-expert score blocks (two per CU), then selection; each block

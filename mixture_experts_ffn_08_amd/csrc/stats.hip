@@ -12,18 +12,15 @@
 // does everything in one launch.  No atomics: results are deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "stats_partial.h"
 #include "stats_single.h"
 
 namespace moe {
 namespace {
 
-// Thread groups for the per-expert sums: G = 256 / E groups of E threads (one
-// group when E > 128); group g takes every G-th item, and the G partial sums are
-// added in group order.
-__device__ __forceinline__ int expert_groups(int E) { return E > 128 ? 1 : 256 / E; }
-
 // Block-wide finish: thread e < E holds sum_t softmax(s_t)_e in fp64.  Writes f, P,
-// L_aux = alpha E sum_e f_e P_e and max/mean = E max_e counts_e / (T k).
+// L_aux = alpha E sum_e f_e P_e and max/mean = E max_e counts_e / (T k).  Called by
+// every thread of a block of at least 256 threads.
 __device__ void finish_stats(double sum, const int32_t* __restrict__ counts, int T, int k, int E, float alpha,
                              float* __restrict__ f, float* __restrict__ P, float* __restrict__ l_aux,
                              float* __restrict__ max_over_mean) {
@@ -41,8 +38,10 @@ __device__ void finish_stats(double sum, const int32_t* __restrict__ counts, int
     P[e] = p;
     fp = (double)fi * (double)p;
   }
-  s_fp[e] = fp;
-  s_max[e] = c;
+  if (e < 256) {  // every thread of the block reaches the barriers below
+    s_fp[e] = fp;
+    s_max[e] = c;
+  }
   __syncthreads();
   for (int h = 128; h > 0; h >>= 1) {
     if (e < h) {
@@ -81,38 +80,7 @@ __global__ __launch_bounds__(256) void stats_partial_kernel(const float* __restr
   for (int j = 0; j < kMaxPerThread; ++j)
     if (tid + 256 * j < n) tile[tid + 256 * j] = v[j];
   __syncthreads();
-  // Softmax normalizers; the exponentials use the hardware exp2 (relative error
-  // about 1e-6, far inside what P is compared to).
-  const int r = lane & 15;
-  for (int lt = wave * 4 + (lane >> 4); lt < kStatsTokens; lt += 16) {  // 16 tokens per pass
-    float m = -INFINITY;
-    if (lt < nt)
-      for (int e = r; e < E; e += 16) m = fmaxf(m, tile[lt * E + e]);
-    m = row16_max(m);
-    float z = 0.f;
-    if (lt < nt)
-      for (int e = r; e < E; e += 16) z += __expf(tile[lt * E + e] - m);
-    z = row16_sum(z);
-    if (r == 0 && lt < nt) {
-      s_max[lt] = m;
-      s_inv[lt] = 1.f / z;
-    }
-  }
-  __syncthreads();
-  const int G = expert_groups(E);
-  const int g = tid / E, e = tid % E;
-  if (g < G) {
-    float part = 0.f;
-#pragma unroll 4
-    for (int lt = g; lt < nt; lt += G) part += __expf(tile[lt * E + e] - s_max[lt]) * s_inv[lt];
-    red[tid] = part;
-  }
-  __syncthreads();
-  if (tid < E) {
-    float acc = red[tid];
-    for (int q = 1; q < G; ++q) acc += red[q * E + tid];
-    partial[(size_t)blockIdx.x * E + tid] = acc;
-  }
+  block_softmax_sums<256>(tile, E, nt, E, s_max, s_inv, red, partial + (size_t)blockIdx.x * E);
 }
 
 // All T <= 64 tokens in one block of 16 waves (stats_single).
@@ -129,14 +97,14 @@ __global__ __launch_bounds__(1024) void stats_small_kernel(const float* __restri
 // fp64, 16 loads in flight (indices clamped, out-of-range terms zeroed, no
 // branch around a load); the group sums are added in group order.  Then f, P,
 // L_aux and max/mean.  No atomics: results are deterministic.
-__global__ __launch_bounds__(256) void stats_final_kernel(const int32_t* __restrict__ counts,
-                                                           const float* __restrict__ partial, int nblk, int T,
-                                                           int k, int E, float alpha, float* __restrict__ f,
-                                                           float* __restrict__ P, float* __restrict__ l_aux,
-                                                           float* __restrict__ max_over_mean) {
-  __shared__ double s_part[256];
+__global__ __launch_bounds__(1024) void stats_final_kernel(const int32_t* __restrict__ counts,
+                                                            const float* __restrict__ partial, int nblk, int T,
+                                                            int k, int E, float alpha, float* __restrict__ f,
+                                                            float* __restrict__ P, float* __restrict__ l_aux,
+                                                            float* __restrict__ max_over_mean) {
+  __shared__ double s_part[1024];
   const int tid = threadIdx.x;
-  const int G = expert_groups(E);
+  const int G = 1024 / E;  // groups of E threads (4 at E = 256, 8 at E = 128)
   const int g = tid / E, ge = tid % E;
   if (g < G) {
     double part[16];
@@ -193,8 +161,12 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   hipLaunchKernelGGL(stats_partial_kernel, dim3(nblk), dim3(256), 0, stream, a.logits, a.T, a.E, a.partial);
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(256), 0, stream, a.counts, a.partial, nblk, a.T, a.k,
-                     a.E, a.alpha, a.f, a.P, a.l_aux, a.max_over_mean);
+  return launch_stats_final(a, stream);
+}
+
+hipError_t launch_stats_final(const StatsArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(1024), 0, stream, a.counts, a.partial, stats_blocks(a.T),
+                     a.T, a.k, a.E, a.alpha, a.f, a.P, a.l_aux, a.max_over_mean);
   return hipGetLastError();
 }
 
