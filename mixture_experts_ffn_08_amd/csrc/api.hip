@@ -478,13 +478,16 @@ int layer_calls(const moe_layer_args& L, hipStream_t stream, bool check) {
     moe::RouteArgs r{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,
                      L.renorm ? 1 : 0, L.logits, L.topk_idx, L.topk_w, L.near_tie, block_counts, stats_partial};
     CHECK(hip_status(moe::launch_route(r, stream), "moe_layer_forward"));
-    moe::PermuteArgs pa{L.topk_idx, L.T, L.k, L.E, L.capacity < 0 ? -1 : L.capacity, L.x, L.d * elem_bytes(L.dtype),
-                        L.counts, L.offsets, L.row_of, L.perm_token, nullptr, block_counts, block_base, 0, 1};
-    CHECK(hip_status(moe::launch_permute(pa, stream), "moe_layer_forward"));
-    // the router wrote the statistics' partial sums: their final reduction needs
-    // only the counts, so it runs here (one block) and no side stream is used
+    // The router wrote the statistics' partial sums: their final reduction needs
+    // only the counts.  It runs as one more block of the dispatch's rank launch,
+    // or right after the dispatch; no side stream is used.
     moe::StatsArgs sa{L.counts, L.logits, L.T, L.k, L.E, L.alpha, L.f, L.P, L.l_aux, L.max_over_mean, stats_partial};
-    CHECK(hip_status(moe::launch_stats_final(sa, stream), "moe_layer_forward"));
+    const bool fuse = moe::permute_fuses_stats(L.T, L.k);
+    moe::PermuteArgs pa{L.topk_idx, L.T, L.k, L.E, L.capacity < 0 ? -1 : L.capacity, L.x, L.d * elem_bytes(L.dtype),
+                        L.counts, L.offsets, L.row_of, L.perm_token, nullptr, block_counts, block_base, 0, 1,
+                        fuse ? &sa : nullptr};
+    CHECK(hip_status(moe::launch_permute(pa, stream), "moe_layer_forward"));
+    if (!fuse) CHECK(hip_status(moe::launch_stats_final(sa, stream), "moe_layer_forward"));
   }
   if (!check && fused) {
     moe::RouteDispatchArgs a{{L.x, L.w_router, L.logit_bias, L.select_bias, L.dtype, L.T, L.d, L.E, L.k, L.mode,

@@ -46,6 +46,21 @@ hipError_t launch_route_dispatch_small(const RouteDispatchArgs& a, hipStream_t s
 hipError_t launch_bias_update(const int32_t* counts, int T, int k, int E, float rate, float* bias,
                               hipStream_t stream);
 
+constexpr int kStatsTokens = 64;  // tokens per partial-sum block
+__host__ __device__ inline int stats_blocks(int T) { return (T + kStatsTokens - 1) / kStatsTokens; }
+
+struct StatsArgs {
+  const int32_t* counts;
+  const float* logits;
+  int T, k, E;
+  float alpha;
+  float *f, *P, *l_aux, *max_over_mean;
+  float* partial;  // workspace [nblk][E]
+};
+hipError_t launch_stats(const StatsArgs& a, hipStream_t stream);
+// The final reduction alone, over stats_blocks(T) partial rows another kernel wrote.
+hipError_t launch_stats_final(const StatsArgs& a, hipStream_t stream);
+
 // Dispatch works on the flattened assignment index p = t*k + j in blocks of
 // kPairsPerBlock assignments.
 constexpr int kPairsPerBlock = 512;
@@ -66,8 +81,13 @@ struct PermuteArgs {
   int32_t* block_base;    // workspace [nblk][E]
   int padded;             // 1: slot e * capacity + rank, offsets e * capacity, padding -1 / zero rows
   int hist_given = 0;     // 1: block_counts already hold the per-block histograms (the router wrote them)
+  // With permute_fuses_stats: the statistics' final reduction over stats->partial
+  // (rows another kernel wrote) runs as one more block of the rank launch.
+  const StatsArgs* stats = nullptr;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// Whether launch_permute runs a given final statistics reduction inside its rank launch.
+bool permute_fuses_stats(int T, int k);
 // Whether launch_route with a block_hist writes the dispatch's per-block histograms
 // for these sizes (its blocks of 64 tokens then hold exactly kPairsPerBlock assignments).
 bool route_writes_block_hist(int dtype, int T, int E, int k);
@@ -114,19 +134,6 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
-constexpr int kStatsTokens = 64;  // tokens per partial-sum block
-inline int stats_blocks(int T) { return (T + kStatsTokens - 1) / kStatsTokens; }
 
-struct StatsArgs {
-  const int32_t* counts;
-  const float* logits;
-  int T, k, E;
-  float alpha;
-  float *f, *P, *l_aux, *max_over_mean;
-  float* partial;  // workspace [nblk][E]
-};
-hipError_t launch_stats(const StatsArgs& a, hipStream_t stream);
-// The final reduction alone, over stats_blocks(T) partial rows another kernel wrote.
-hipError_t launch_stats_final(const StatsArgs& a, hipStream_t stream);
 
 }  // namespace moe

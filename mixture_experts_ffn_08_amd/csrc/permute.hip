@@ -23,6 +23,7 @@
 #include "common.h"
 #include "dispatch_single.h"
 #include "kernels.h"
+#include "stats_partial.h"
 
 namespace moe {
 namespace {
@@ -168,9 +169,10 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
                                                          const int32_t* __restrict__ block_counts, int nblk, int ep,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ row_of,
-                                                         int32_t* __restrict__ perm_token) {
+                                                         int32_t* __restrict__ perm_token, StatsArgs st) {
   __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
   __shared__ int part_base[kBP], part_total[kBP];
+  __shared__ int32_t s_tot[MOE_MAX_EXPERTS];
   __shared__ int base_s[MOE_MAX_EXPERTS], kept_s[MOE_MAX_EXPERTS], incl[2][MOE_MAX_EXPERTS];
   constexpr int kBatch = 16;  // loads in flight per thread
   const int tid = threadIdx.x;
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
   const int b0 = min(c * chunk, nblk), b1 = e2 < E ? min(b0 + chunk, nblk) : b0;
   const int ec = e2 < E ? e2 : 0;
   const int me = blockIdx.x;
-  int sb = 0, st = 0;
+  int sb = 0, stot = 0;
   for (int b = b0; b < b1; b += kBatch) {
     int v[kBatch];
 #pragma unroll
@@ -191,13 +193,26 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int x = b + q < b1 ? v[q] : 0;
-      st += x;
+      stot += x;
       sb += b + q < me ? x : 0;
     }
   }
   part_base[tid] = sb;
-  part_total[tid] = st;
+  part_total[tid] = stot;
   __syncthreads();
+  if (me == nblk) {
+    // the extra block (uniform): the totals are the counts; then the statistics'
+    // final reduction over the partial rows the router wrote
+    if (tid < E) {
+      int total = 0;
+      for (int q = 0; q < nch; ++q) total += part_total[q * ep + tid];
+      s_tot[tid] = total;
+    }
+    __syncthreads();
+    stats_final_block<kBP>(s_tot, st.partial, stats_blocks(st.T), st.T, k, E, st.alpha, st.f, st.P, st.l_aux,
+                           st.max_over_mean);
+    return;
+  }
   const int64_t p = (int64_t)blockIdx.x * kBP + tid;
   const int e = p < P ? idx[p] : -1;
   const bool valid = (unsigned)e < (unsigned)E;
@@ -291,6 +306,11 @@ __global__ __launch_bounds__(kBP) void permute_single_kernel(const int32_t* __re
 
 }  // namespace
 
+bool permute_fuses_stats(int T, int k) {
+  const int nblk = permute_blocks(T, k);
+  return MOE_RANK_SCAN && nblk > 1 && nblk <= kRankScanMaxBlocks;
+}
+
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int64_t P = (int64_t)a.T * a.k;
   const int nblk = permute_blocks(a.T, a.k);
@@ -303,8 +323,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   } else if (nblk <= kRankScanMaxBlocks && MOE_RANK_SCAN) {
     if (!a.hist_given)
       hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);
-    hipLaunchKernelGGL(rank_scan_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.k, a.E, a.capacity,
-                       a.padded, a.block_counts, nblk, ep, a.counts, a.offsets, a.row_of, a.perm_token);
+    // with a final statistics reduction, one more block (index nblk) runs it
+    const StatsArgs st = a.stats != nullptr ? *a.stats : StatsArgs{};
+    hipLaunchKernelGGL(rank_scan_kernel, dim3(nblk + (a.stats != nullptr ? 1 : 0)), dim3(kBP), 0, stream,
+                       a.topk_idx, P, a.k, a.E, a.capacity, a.padded, a.block_counts, nblk, ep, a.counts, a.offsets,
+                       a.row_of, a.perm_token, st);
   } else {
     if (!a.hist_given)
       hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kBP), 0, stream, a.topk_idx, P, a.E, a.block_counts);

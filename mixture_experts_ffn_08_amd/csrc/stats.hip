@@ -18,44 +18,6 @@
 namespace moe {
 namespace {
 
-// Block-wide finish: thread e < E holds sum_t softmax(s_t)_e in fp64.  Writes f, P,
-// L_aux = alpha E sum_e f_e P_e and max/mean = E max_e counts_e / (T k).  Called by
-// every thread of a block of at least 256 threads.
-__device__ void finish_stats(double sum, const int32_t* __restrict__ counts, int T, int k, int E, float alpha,
-                             float* __restrict__ f, float* __restrict__ P, float* __restrict__ l_aux,
-                             float* __restrict__ max_over_mean) {
-  __shared__ double s_fp[256];
-  __shared__ int s_max[256];
-  const int e = threadIdx.x;
-  const float tk = (float)((int64_t)T * k);
-  double fp = 0.0;
-  int c = 0;
-  if (e < E) {
-    const float p = (float)(sum / (double)T);
-    c = counts[e];
-    const float fi = (float)c / tk;
-    f[e] = fi;
-    P[e] = p;
-    fp = (double)fi * (double)p;
-  }
-  if (e < 256) {  // every thread of the block reaches the barriers below
-    s_fp[e] = fp;
-    s_max[e] = c;
-  }
-  __syncthreads();
-  for (int h = 128; h > 0; h >>= 1) {
-    if (e < h) {
-      s_fp[e] += s_fp[e + h];
-      s_max[e] = max(s_max[e], s_max[e + h]);
-    }
-    __syncthreads();
-  }
-  if (e == 0) {
-    *l_aux = (float)((double)alpha * (double)E * s_fp[0]);
-    *max_over_mean = (float)((int64_t)E * s_max[0]) / tk;
-  }
-}
-
 // One block per 64 tokens.  The block's 64 x E score tile is copied to LDS with
 // all loads in flight; each 16-lane row of a wave then takes one token (max and
 // sum of exponentials with DPP butterflies); finally thread (g, e) sums
@@ -93,42 +55,12 @@ __global__ __launch_bounds__(1024) void stats_small_kernel(const float* __restri
   stats_single(logits, T, E, counts, k, alpha, f, P, l_aux, max_over_mean);
 }
 
-// One block.  Thread (g, e) sums partial[b][e] over blocks b = g, g + G, ... in
-// fp64, 16 loads in flight (indices clamped, out-of-range terms zeroed, no
-// branch around a load); the group sums are added in group order.  Then f, P,
-// L_aux and max/mean.  No atomics: results are deterministic.
-__global__ __launch_bounds__(1024) void stats_final_kernel(const int32_t* __restrict__ counts,
-                                                            const float* __restrict__ partial, int nblk, int T,
-                                                            int k, int E, float alpha, float* __restrict__ f,
-                                                            float* __restrict__ P, float* __restrict__ l_aux,
-                                                            float* __restrict__ max_over_mean) {
-  __shared__ double s_part[1024];
-  const int tid = threadIdx.x;
-  const int G = 1024 / E;  // groups of E threads (4 at E = 256, 8 at E = 128)
-  const int g = tid / E, ge = tid % E;
-  if (g < G) {
-    double part[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) part[q] = 0.0;
-    for (int b0 = g; b0 < nblk; b0 += 16 * G) {
-      float pv[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) pv[q] = partial[(size_t)min(b0 + q * G, nblk - 1) * E + ge];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) part[q] += b0 + q * G < nblk ? (double)pv[q] : 0.0;
-    }
-    double sum = 0.0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) sum += part[q];
-    s_part[tid] = sum;
-  }
-  __syncthreads();
-  double sum = 0.0;
-  if (tid < E) {
-    sum = s_part[tid];
-    for (int q = 1; q < G; ++q) sum += s_part[q * E + tid];
-  }
-  finish_stats(sum, counts, T, k, E, alpha, f, P, l_aux, max_over_mean);
+// One block: stats_final_block.
+__global__ __launch_bounds__(kStatsFinalThreads) void stats_final_kernel(
+    const int32_t* __restrict__ counts, const float* __restrict__ partial, int nblk, int T, int k, int E,
+    float alpha, float* __restrict__ f, float* __restrict__ P, float* __restrict__ l_aux,
+    float* __restrict__ max_over_mean) {
+  stats_final_block<kStatsFinalThreads>(counts, partial, nblk, T, k, E, alpha, f, P, l_aux, max_over_mean);
 }
 
 // Bias balancing (The Residual Stream, "Keeping the load even", and the MoE
@@ -165,7 +97,8 @@ hipError_t launch_stats(const StatsArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_stats_final(const StatsArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(1024), 0, stream, a.counts, a.partial, stats_blocks(a.T),
+  hipLaunchKernelGGL(stats_final_kernel, dim3(1), dim3(kStatsFinalThreads), 0, stream, a.counts, a.partial,
+                     stats_blocks(a.T),
                      a.T, a.k, a.E, a.alpha, a.f, a.P, a.l_aux, a.max_over_mean);
   return hipGetLastError();
 }
