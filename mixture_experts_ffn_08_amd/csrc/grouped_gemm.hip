@@ -96,8 +96,7 @@ struct TileScan {
   int wave_tot[4];
 };
 
-// Block-wide: per-group m-tile counts, their inclusive prefix and the clamped group
-// bounds; returns the total.
+
 // The rest of a round of a k slice's pattern: its other MPR - 1 MFMAs, each
 // after its share of the round's N LDS operations (spread one or two at a time
 // between MFMAs rather than bunched after the first).
@@ -111,13 +110,16 @@ __device__ __forceinline__ void lds_slots() {
   }
 }
 
+// Block-wide: per-group m-tile counts, their inclusive prefix and the clamped group
+// bounds; returns the total.  Groups of at most min_rows rows hold no tiles (the
+// weight-streaming kernel takes them).
 template <int BM>
-__device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, TileScan& s) {
+__device__ int scan_tiles(const int32_t* __restrict__ offsets, int G, int max_rows, int min_rows, TileScan& s) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int cnt = 0;
   if (tid < G) {
     const int lo = clamp_off(offsets[tid], max_rows), hi = clamp_off(offsets[tid + 1], max_rows);
-    cnt = hi > lo ? (hi - lo + BM - 1) / BM : 0;
+    cnt = hi - lo > min_rows ? (hi - lo + BM - 1) / BM : 0;
     s.start[tid] = lo;
     if (tid == G - 1) s.start[G] = hi;
   }
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, int n_tiles, const int32_t* __restrict__ out_tok,
-    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out) {
+    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out, int min_rows) {
   static_assert(!(SCATTER && DUAL), "the scatter form is single");
   constexpr int STAGE = (BM + BN) * LDS_STRIDE;  // bf16 elements per LDS stage (A rows, then B rows)
   constexpr int NAC = BM / 32;                   // A chunks per thread per K step
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   __shared__ TileScan scan;
   __shared__ int tile_rows[256];  // gather: row indices of the tile being set up
 
-  const int total = scan_tiles<BM>(offsets, G, max_rows, scan) * n_tiles;
+  const int total = scan_tiles<BM>(offsets, G, max_rows, min_rows, scan) * n_tiles;
   // Persistent schedule.  Hardware block b runs on XCD b % 8 (blocks are dealt
   // round-robin); XCD x owns the contiguous tile run [x per, (x + 1) per) and its
   // blocks take the run's tiles in turn, so the CUs of an XCD work on neighbouring
@@ -610,27 +612,28 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 // k-step u of a 128-wide K chunk, lane group q = l / 16 holds k values
 // 32 u + 8 q .. 32 u + 8 q + 7 of its row (the instruction's own order), so each
 // 16-byte load instruction reads 64 contiguous bytes of 16 rows.  Two chunks are
-// in flight per wave.
+// in flight per wave.  A weight pass serves TT 16-row token tiles (the launcher uses
+// one, and gives groups of more rows to the tiled kernel).
 constexpr int SK_ROWS = 16;   // B rows per MFMA tile
 // B rows per block: dual, 4 waves x 16 rows (each with its gate and up rows);
 // single, 4 waves x 32 rows (two 16-row sets).
 __host__ __device__ constexpr int sk_bn(bool dual) { return dual ? 64 : 128; }
 constexpr int SK_CHUNK = 128; // K per chunk
-constexpr int kSkinnyTwoTilesAbove = 10;  // rows per group (average) above which a pass takes two token tiles
 
 template <bool DUAL, bool GATHER, int TT, bool SCATTER = false>
 __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
-    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const int32_t* __restrict__ out_tok = nullptr,
-    const float* __restrict__ out_w = nullptr, float* __restrict__ y_acc = nullptr, int T_out = 0) {
+    const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const int32_t* __restrict__ out_tok,
+    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out, int big_rows) {
   static_assert(!(SCATTER && DUAL), "the scatter form is single");
   const int nblk_n = N / sk_bn(DUAL);
   // each XCD streams one contiguous eighth of the weights
   const int lb = xcd_contiguous_block();
   const int g = lb / nblk_n, nb = lb % nblk_n;
   const int lo = clamp_off(offsets[g], max_rows), hi = clamp_off(offsets[g + 1], max_rows);
-  if (hi <= lo) return;
+  // empty groups, and groups of more than big_rows rows (the tiled kernel takes those)
+  if (hi <= lo || hi - lo > big_rows) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, q = lane >> 4;
   const int n_base = nb * sk_bn(DUAL) + wave * (DUAL ? SK_ROWS : 2 * SK_ROWS);
@@ -825,61 +828,28 @@ int persistent_blocks() {
   return cached[dev];
 }
 
-hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
+namespace {
+
+// The tiled kernel with bm-row tiles over the groups of more than min_rows rows.
+hipError_t launch_tiled(const GroupedGemmArgs& a, bool dual, int bm, int min_rows, hipStream_t stream) {
   const bool scatter = a.y_acc != nullptr;
-  if (scatter && (dual || a.a_rows != nullptr)) return hipErrorInvalidValue;
-  if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
-    // few rows per group on average: stream the weights, skip the 256-row tiles
-    const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
-#define MOE_SKINNY(D, GA, TT)                                                                                \
-  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA, TT>), grid, block, 0, stream, (const uint16_t*)a.A, \
-                     a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,     \
-                     D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C)
-#define MOE_SKINNY_SCATTER(TT)                                                                                \
-  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<false, false, TT, true>), grid, block, 0, stream,           \
-                     (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
-                     (const uint16_t*)a.B0, nullptr, nullptr, a.out_tok, a.out_w, a.y_acc, a.T)
-    const bool gather = a.a_rows != nullptr;
-    if (scatter) {
-      // the scatter form runs on the down GEMM: single, no gather
-      if ((int64_t)a.max_rows > (int64_t)kSkinnyTwoTilesAbove * a.G) MOE_SKINNY_SCATTER(2);
-      else MOE_SKINNY_SCATTER(1);
-      return hipGetLastError();
-    }
-#undef MOE_SKINNY_SCATTER
-    // two 16-row token tiles per weight pass once groups average over 10 rows (then
-    // many groups exceed 16 rows, and one tile per pass would stream their weights twice)
-    if ((int64_t)a.max_rows > (int64_t)kSkinnyTwoTilesAbove * a.G) {
-      if (dual && gather) MOE_SKINNY(true, true, 2);
-      else if (dual) MOE_SKINNY(true, false, 2);
-      else if (gather) MOE_SKINNY(false, true, 2);
-      else MOE_SKINNY(false, false, 2);
-    } else {
-      if (dual && gather) MOE_SKINNY(true, true, 1);
-      else if (dual) MOE_SKINNY(true, false, 1);
-      else if (gather) MOE_SKINNY(false, true, 1);
-      else MOE_SKINNY(false, false, 1);
-    }
-#undef MOE_SKINNY
-    return hipGetLastError();
-  }
-  if (a.dtype == MOE_BF16) {
-    const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
-    const int64_t rows_per_group = (a.max_rows + a.G - 1) / a.G;  // ceiling of the average
-    const int bm = rows_per_group <= kSmallTileRowsPerGroup ? 128 : rows_per_group <= kMidTileRowsPerGroup ? 192 : 256;
-    const int64_t m_tiles = (a.max_rows + bm - 1) / bm + std::min(a.G, a.max_rows);
-    // persistent grid: one block per CU (the LDS stages take a CU), a multiple of
-    // the 8 XCDs, no more than the tiles there can be
-    const int64_t max_tiles = m_tiles * n_tiles;
-    if (max_tiles <= 0) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
-    // Step 2 of a tile can be loaded in the previous tile's epilogue when there is one (K >= 256).
-    const bool early = a.K >= 4 * BK;
+  const int n_tiles = dual ? a.N / (BN / 2) : (a.N + BN - 1) / BN;
+  // m-tiles: at most ceil(rows / bm) + 1 per group that holds tiles, and at most
+  // max_rows / (min_rows + 1) groups hold more than min_rows rows
+  const int64_t groups = std::min<int64_t>(a.G, (int64_t)a.max_rows / ((int64_t)min_rows + 1));
+  const int64_t m_tiles = (a.max_rows + bm - 1) / bm + groups;
+  // persistent grid: one block per CU (the LDS stages take a CU), a multiple of
+  // the 8 XCDs, no more than the tiles there can be
+  const int64_t max_tiles = m_tiles * n_tiles;
+  if (max_tiles <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(persistent_blocks(), (max_tiles + kXcds - 1) / kXcds * kXcds);
+  // Step 2 of a tile can be loaded in the previous tile's epilogue when there is one (K >= 256).
+  const bool early = a.K >= 4 * BK;
 #define MOE_TILED_E(D, M, E, S)                                                                               \
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<D, M, E, S>), dim3((unsigned)blocks), dim3(256), 0, stream,   \
                      (const uint16_t*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,         \
                      (const uint16_t*)a.B0, D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, n_tiles,     \
-                     a.out_tok, a.out_w, a.y_acc, a.T)
+                     a.out_tok, a.out_w, a.y_acc, a.T, min_rows)
 #define MOE_TILED(D, M)                                     \
   do {                                                      \
     if (early) {                                            \
@@ -892,27 +862,63 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
       else MOE_TILED_E(false, M, false, false);             \
     }                                                       \
   } while (0)
-    if (bm == 128) {
-      if (dual) MOE_TILED(true, 128); else MOE_TILED(false, 128);
-    } else if (bm == 192) {
-      if (dual) MOE_TILED(true, 192); else MOE_TILED(false, 192);
-    } else {
-      if (dual) MOE_TILED(true, 256); else MOE_TILED(false, 256);
-    }
+  if (bm == 128) {
+    if (dual) MOE_TILED(true, 128); else MOE_TILED(false, 128);
+  } else if (bm == 192) {
+    if (dual) MOE_TILED(true, 192); else MOE_TILED(false, 192);
+  } else {
+    if (dual) MOE_TILED(true, 256); else MOE_TILED(false, 256);
+  }
 #undef MOE_TILED
 #undef MOE_TILED_E
-  } else {
-    const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;
-    if (blocks <= 0) return hipSuccess;
-    if (dual)
-      hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const float*)a.B0, (const float*)a.B1, (float*)a.C, nullptr, nullptr, nullptr, 0);
-    else
-      hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
-                         (const float*)a.B0, nullptr, (float*)a.C, a.out_tok, a.out_w, a.y_acc, a.T);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream) {
+  const bool scatter = a.y_acc != nullptr;
+  if (scatter && (dual || a.a_rows != nullptr)) return hipErrorInvalidValue;
+  if (a.dtype == MOE_BF16 && (int64_t)a.max_rows <= (int64_t)kSkinnyRowsPerGroup * a.G) {
+    // Few rows per group on average: the weight-streaming kernel takes the groups
+    // of up to 16 rows (one 16-row token tile, one pass over their weights), and
+    // the tiled kernel, with 128-row tiles, the larger ones.  Group sizes are known
+    // only on the device, so both launches read the offsets; the second is issued
+    // when some group can exceed 16 rows.  A skewed routing (a hot expert holding
+    // most tokens) would otherwise stream the hot expert's weights once per 16 of
+    // its rows, one pass after another in the same blocks.
+    const int big = SK_ROWS;
+    const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
+#define MOE_SKINNY(D, GA, S)                                                                                    \
+  hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA, 1, S>), grid, block, 0, stream, (const uint16_t*)a.A, \
+                     a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,       \
+                     D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, a.out_tok, a.out_w, a.y_acc, a.T, big)
+    const bool gather = a.a_rows != nullptr;
+    if (scatter) MOE_SKINNY(false, false, true);
+    else if (dual && gather) MOE_SKINNY(true, true, false);
+    else if (dual) MOE_SKINNY(true, false, false);
+    else if (gather) MOE_SKINNY(false, true, false);
+    else MOE_SKINNY(false, false, false);
+#undef MOE_SKINNY
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_rows <= big) return e;
+    return launch_tiled(a, dual, 128, big, stream);
   }
+  if (a.dtype == MOE_BF16) {
+    const int64_t rows_per_group = (a.max_rows + a.G - 1) / a.G;  // ceiling of the average
+    const int bm = rows_per_group <= kSmallTileRowsPerGroup ? 128 : rows_per_group <= kMidTileRowsPerGroup ? 192 : 256;
+    return launch_tiled(a, dual, bm, 0, stream);
+  }
+  const int64_t blocks = ((int64_t)a.max_rows * a.N + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  if (dual)
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                       (const float*)a.B0, (const float*)a.B1, (float*)a.C, nullptr, nullptr, nullptr, 0);
+  else
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const float*)a.A, a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K,
+                       (const float*)a.B0, nullptr, (float*)a.C, a.out_tok, a.out_w, a.y_acc, a.T);
   return hipGetLastError();
 }
 

@@ -111,8 +111,9 @@ struct GroupedGemmArgs {
   int T = 0;
 };
 // dual = true: C = SiLU(A B0^T) * (A B1^T); dual = false: C = A B0^T.
-// bf16 launches with max_rows <= kSkinnyRowsPerGroup * G use the skinny kernel.
-constexpr int kSkinnyRowsPerGroup = 16;
+// bf16 launches with max_rows <= kSkinnyRowsPerGroup * G use the skinny kernel for
+// the groups of up to 16 rows and the tiled kernel for the others.
+constexpr int kSkinnyRowsPerGroup = 8;
 hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t stream);
 
 // Around the scatter form of the down GEMM: zero y_acc [T][d] and write

@@ -451,9 +451,11 @@ def test_zero_tokens_is_a_no_op():
     ("bf16", [0, 1, 63, 64, 65, 127, 128, 129, 3]),            # small groups: 128-row tiles
     ("bf16", [0, 1, 191, 192, 193, 150, 128, 129, 64]),        # mid-size groups: 192-row tiles
     ("f32", [0, 1, 127, 128, 129, 300]),
-    ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7]),  # few rows per group: skinny kernel,
-                                                                # two token tiles per weight pass
-    ("bf16", [0, 1, 3, 16, 17, 2, 0, 5]),                      # skinny, one token tile per pass
+    # few rows per group on average: groups of up to 16 rows on the skinny kernel, the
+    # larger ones (17 .. 64 rows) on 128-row tiles, in one call
+    ("bf16", [0, 1, 3, 16, 17, 0, 31, 33, 64, 2, 5, 0, 40, 7] + [0] * 18),
+    ("bf16", [0, 1, 3, 16, 2, 0, 5, 16]),                      # skinny only; the tiled launch finds no group
+    ("bf16", [0, 1, 3, 5, 2]),                                 # skinny only, no tiled launch (max_rows <= 16)
 ])
 def test_grouped_gemm_hand_made_groups(dtype, sizes):
     """Ragged groups (empty, single row, tile edges), rows left outside every group,
