@@ -23,14 +23,23 @@ pytestmark = pytest.mark.gpu
 
 CONFIGS = ["tiny_f32", "mixtral", "mixtral_cap", "qwen2", "qwen3_prefill", "qwen3_decode", "dsv3_skew",
            # dropping at full size: the configured phi = 1.25 drops nothing at seed 0, these do
-           "mixtral_phi1.0", "mixtral_phi0.5", "tiny_f32_phi1.25"]
+           "mixtral_phi1.0", "mixtral_phi0.5", "tiny_f32_phi1.25",
+           # a decode batch on the skewed DeepSeek-shaped layer: a few rows per expert on average,
+           # hot experts with up to 64 rows (weight-streaming kernel and 128-row tiles in one call)
+           "dsv3_skew_T64"]
 
 
 def config_shape(name):
-    """A configured shape, or one with another capacity factor ("<shape>_phi<phi>")."""
+    """A configured shape, or one with another capacity factor ("<shape>_phi<phi>") or
+    token count ("<shape>_T<T>")."""
     base, _, phi = name.partition("_phi")
+    base, _, tokens = base.partition("_T")
     s = minp.SHAPES[base]
-    return s if not phi else s.with_(phi=float(phi), name=name)
+    if phi:
+        s = s.with_(phi=float(phi), name=name)
+    if tokens:
+        s = s.with_(T=int(tokens), name=name)
+    return s
 
 
 def weights_by_expert(idx_gpu, idx_ref, w_ref, ok):
