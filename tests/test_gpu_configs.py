@@ -159,13 +159,14 @@ def test_config_parity(name):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_skew", "mixtral_cap", "qwen3_decode"])
+@pytest.mark.parametrize("name", ["qwen3_prefill", "dsv3_skew", "mixtral_cap", "qwen3_decode", "dsv3_skew_T64"])
 def test_scatter_combine_full_size(name):
     """At full size, in the launch configuration of the timed layer: the scatter
     combine (weighted sum in the down GEMM's epilogue) against the gather combine,
-    y one rounding of the same sum apart on every token.  The gather path's y is
-    compared with the oracle in full by test_config_parity."""
-    shape = minp.SHAPES[name]
+    y one rounding of the same sum apart on every token (dsv3_skew_T64: the skinny
+    and the tiled scatter forms in one call).  The gather path's y is compared with
+    the oracle in full by test_config_parity."""
+    shape = config_shape(name)
     inp = minp.LayerInputs(shape, seed=0)
     run = LayerRun(inp)
     try:
