@@ -59,6 +59,7 @@ def parse():
 # this summary, together with a hash of the kernel sources they were taken on; they
 # are reported only while the sources are unchanged.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_gemm_qwen3_prefill_pmc.txt")
+CLOCK_SUMMARY = os.path.join(ROOT, "profiles", "grouped_gemm_qwen3_prefill_mfma_l2.txt")
 GEMM_SOURCES = ("mixture_experts_ffn_08_amd/csrc/grouped_gemm.hip", "mixture_experts_ffn_08_amd/csrc/common.h",
                 "mixture_experts_ffn_08_amd/csrc/kernels.h")
 
@@ -94,12 +95,10 @@ def recorded_traffic():
 def recorded_clocks():
     """Sustained clocks (GHz) of the gate/up and down launches from the counter
     summary, or None if there is none or the kernel sources changed since."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "grouped_gemm_qwen3_prefill_mfma_l2.txt")
-    if not os.path.exists(path):
+    if not os.path.exists(CLOCK_SUMMARY):
         return None
     fields = {}
-    with open(path) as f:
+    with open(CLOCK_SUMMARY) as f:
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 key, _, val = line.partition("=")
