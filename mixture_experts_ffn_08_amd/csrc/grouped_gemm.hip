@@ -619,18 +619,30 @@ constexpr int SK_ROWS = 16;   // B rows per MFMA tile
 // single, 4 waves x 32 rows (two 16-row sets).
 __host__ __device__ constexpr int sk_bn(bool dual) { return dual ? 64 : 128; }
 constexpr int SK_CHUNK = 128; // K per chunk
+constexpr int64_t kSliceDealBytes = 16ll << 20;  // per expert weight matrix, for slice dealing
 
 template <bool DUAL, bool GATHER, int TT, bool SCATTER = false>
 __global__ __launch_bounds__(256) void grouped_gemm_skinny_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ a_rows, int a_nrows,
     const int32_t* __restrict__ offsets, int G, int max_rows, int N, int K, const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, uint16_t* __restrict__ C, const int32_t* __restrict__ out_tok,
-    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out, int big_rows) {
+    const float* __restrict__ out_w, float* __restrict__ y_acc, int T_out, int big_rows, int slice_deal) {
   static_assert(!(SCATTER && DUAL), "the scatter form is single");
   const int nblk_n = N / sk_bn(DUAL);
-  // each XCD streams one contiguous eighth of the weights
-  const int lb = xcd_contiguous_block();
-  const int g = lb / nblk_n, nb = lb % nblk_n;
+  // Each XCD streams one contiguous eighth of the weights (whole experts), or with
+  // slice_deal (nblk_n a multiple of 8) one contiguous eighth of every expert's B
+  // rows: then every touched expert loads the 8 XCDs evenly, however few are
+  // touched, and for large experts the pages an XCD touches are as few.
+  int g, nb;
+  if (slice_deal) {
+    const int per = nblk_n >> 3, slot = (int)blockIdx.x >> 3;
+    g = slot / per;
+    nb = ((int)blockIdx.x & 7) * per + slot % per;
+  } else {
+    const int lb = xcd_contiguous_block();
+    g = lb / nblk_n;
+    nb = lb % nblk_n;
+  }
   const int lo = clamp_off(offsets[g], max_rows), hi = clamp_off(offsets[g + 1], max_rows);
   // empty groups, and groups of more than big_rows rows (the tiled kernel takes those)
   if (hi <= lo || hi - lo > big_rows) return;
@@ -888,11 +900,15 @@ hipError_t launch_grouped_gemm(const GroupedGemmArgs& a, bool dual, hipStream_t 
     // most tokens) would otherwise stream the hot expert's weights once per 16 of
     // its rows, one pass after another in the same blocks.
     const int big = SK_ROWS;
-    const dim3 grid((unsigned)((int64_t)a.G * (a.N / sk_bn(dual)))), block(256);
+    const int nblk_n = a.N / sk_bn(dual);
+    // experts of 16 MB or more per weight matrix: deal each one's B rows to the XCDs
+    const int slice_deal = nblk_n % kXcds == 0 && (int64_t)a.N * a.K * 2 >= (int64_t)kSliceDealBytes;
+    const dim3 grid((unsigned)((int64_t)a.G * nblk_n)), block(256);
 #define MOE_SKINNY(D, GA, S)                                                                                    \
   hipLaunchKernelGGL((grouped_gemm_skinny_kernel<D, GA, 1, S>), grid, block, 0, stream, (const uint16_t*)a.A, \
                      a.a_rows, a.a_nrows, a.offsets, a.G, a.max_rows, a.N, a.K, (const uint16_t*)a.B0,       \
-                     D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, a.out_tok, a.out_w, a.y_acc, a.T, big)
+                     D ? (const uint16_t*)a.B1 : nullptr, (uint16_t*)a.C, a.out_tok, a.out_w, a.y_acc, a.T, big,  \
+                     slice_deal)
     const bool gather = a.a_rows != nullptr;
     if (scatter) MOE_SKINNY(false, false, true);
     else if (dual && gather) MOE_SKINNY(true, true, false);
