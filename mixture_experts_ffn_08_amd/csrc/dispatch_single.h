@@ -16,6 +16,42 @@ namespace moe {
 constexpr int kSingleMaxPairs = 512;             // assignments one block dispatches
 constexpr int kSingleWords = kSingleMaxPairs / 32;  // bitmap words per expert
 
+// Kept counts and their inclusive scan over E <= MOE_MAX_EXPERTS experts, by the
+// block's first wave alone (lane l takes experts 4 l .. 4 l + 3, a shuffle prefix
+// adds the earlier lanes' sums): one barrier afterwards instead of one per step of a
+// block-wide scan.  cnt in LDS; kept and incl (LDS) receive min(cnt, cap) (cnt when
+// dropless) and the inclusive prefix of kept.  Every thread calls it.
+__device__ inline void wave0_kept_scan(const int* __restrict__ cnt, int E, int64_t cap, int* __restrict__ kept,
+                                       int* __restrict__ incl) {
+  static_assert(MOE_MAX_EXPERTS <= 4 * 64, "four experts a lane");
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  int v[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * lane + j;
+    const int c = i < E ? cnt[i] : 0;
+    v[j] = cap < 0 ? c : (int)min((int64_t)c, cap);
+    sum += v[j];
+  }
+  int run = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(run, o, 64);
+    if (lane >= o) run += u;
+  }
+  run -= sum;  // exclusive prefix of this lane's first expert
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * lane + j;
+    run += v[j];
+    if (i < E) {
+      kept[i] = v[j];
+      incl[i] = run;
+    }
+  }
+}
+
 // Called by every thread of a block of at least kSingleMaxPairs threads; P <= 512.
 // idx may be in LDS.  The block's threads exchange data through LDS only, so the
 // barriers wait for LDS operations, not for global stores.  counts_copy (LDS or
@@ -27,7 +63,7 @@ __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t 
   __shared__ uint32_t mask[MOE_MAX_EXPERTS * kSingleWords];
   __shared__ int cnt[MOE_MAX_EXPERTS];
   __shared__ int kept[MOE_MAX_EXPERTS];
-  __shared__ int incl[2][MOE_MAX_EXPERTS];
+  __shared__ int incl[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x, nthr = blockDim.x;
   for (int i = tid; i < E * kSingleWords; i += nthr) mask[i] = 0u;
   for (int i = tid; i < E; i += nthr) cnt[i] = 0;
@@ -44,19 +80,11 @@ __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t 
   for (int i = tid; i < E; i += nthr) {
     counts[i] = cnt[i];
     if (counts_copy != nullptr) counts_copy[i] = cnt[i];
-    kept[i] = cap < 0 ? cnt[i] : (int)min((int64_t)cnt[i], cap);
-    incl[0][i] = kept[i];
   }
+  wave0_kept_scan(cnt, E, cap, kept, incl);
   lds_barrier();
-  // inclusive scan of the kept counts over experts (Hillis-Steele, ping-pong buffers)
-  int src = 0;
-  for (int h = 1; h < E; h <<= 1) {
-    for (int i = tid; i < E; i += nthr) incl[src ^ 1][i] = incl[src][i] + (i >= h ? incl[src][i - h] : 0);
-    lds_barrier();
-    src ^= 1;
-  }
   if (!padded) {
-    for (int i = tid; i < E; i += nthr) offsets[i + 1] = incl[src][i];
+    for (int i = tid; i < E; i += nthr) offsets[i + 1] = incl[i];
     if (tid == 0) offsets[0] = 0;
   }
   if (tid >= P) return;
@@ -66,7 +94,7 @@ __device__ inline void dispatch_single(const int32_t* __restrict__ idx, int64_t 
     int rank = __popc(m[w] & (bit - 1u));
     for (int q = 0; q < w; ++q) rank += __popc(m[q]);
     if (cap < 0 || rank < cap) {
-      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept[e] + rank;
+      row = padded ? (int)(e * cap) + rank : incl[e] - kept[e] + rank;
       perm_token[row] = tid / k;
     }
   }

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
                                                      int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets) {
   __shared__ int part[1024];
-  __shared__ int kept_s[2][MOE_MAX_EXPERTS];
+  __shared__ int tot_s[MOE_MAX_EXPERTS], kept_s[MOE_MAX_EXPERTS], incl_s[MOE_MAX_EXPERTS];
   constexpr int kBatch = 16;  // loads in flight per thread
   const int tid = threadIdx.x;
   // expert fastest (ep >= E, a power of two): a wave reads 64 consecutive experts'
@@ -98,18 +98,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   }
   if (active && c == tpe - 1) {
     counts[e] = base;
-    kept_s[0][e] = cap < 0 ? base : (int)min((int64_t)base, cap);
+    tot_s[e] = base;
   }
   __syncthreads();
-  // inclusive scan of kept counts over experts (Hillis-Steele, ping-pong buffers)
-  int src = 0;
-  for (int h = 1; h < E; h <<= 1) {
-    if (tid < E) kept_s[src ^ 1][tid] = kept_s[src][tid] + (tid >= h ? kept_s[src][tid - h] : 0);
-    __syncthreads();
-    src ^= 1;
-  }
+  // kept counts and their inclusive scan over experts (the first wave)
+  wave0_kept_scan(tot_s, E, cap, kept_s, incl_s);
+  __syncthreads();
   if (!padded) {
-    if (tid < E) offsets[tid + 1] = kept_s[src][tid];
+    if (tid < E) offsets[tid + 1] = incl_s[tid];
     if (tid == 0) offsets[0] = 0;
   }
 }
@@ -173,7 +169,7 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
   __shared__ uint32_t mask[MOE_MAX_EXPERTS * kWords];
   __shared__ int part_base[kBP], part_total[kBP];
   __shared__ int32_t s_tot[MOE_MAX_EXPERTS];
-  __shared__ int base_s[MOE_MAX_EXPERTS], kept_s[MOE_MAX_EXPERTS], incl[2][MOE_MAX_EXPERTS];
+  __shared__ int base_s[MOE_MAX_EXPERTS], kept_s[MOE_MAX_EXPERTS], incl[MOE_MAX_EXPERTS];
   constexpr int kBatch = 16;  // loads in flight per thread
   const int tid = threadIdx.x;
   for (int i = tid; i < E * kWords; i += kBP) mask[i] = 0u;
@@ -226,21 +222,15 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
       total += part_total[q * ep + tid];
     }
     base_s[tid] = base;
-    const int kept = cap < 0 ? total : (int)min((int64_t)total, cap);
-    kept_s[tid] = kept;
-    incl[0][tid] = kept;
+    s_tot[tid] = total;
     if (me == 0) counts[tid] = total;
   }
   __syncthreads();
-  // inclusive scan of the kept totals over experts (Hillis-Steele, ping-pong buffers)
-  int src = 0;
-  for (int h = 1; h < E; h <<= 1) {
-    if (tid < E) incl[src ^ 1][tid] = incl[src][tid] + (tid >= h ? incl[src][tid - h] : 0);
-    __syncthreads();
-    src ^= 1;
-  }
+  // kept totals and their inclusive scan over experts (the first wave)
+  wave0_kept_scan(s_tot, E, cap, kept_s, incl);
+  __syncthreads();
   if (me == 0 && !padded) {
-    if (tid < E) offsets[tid + 1] = incl[src][tid];
+    if (tid < E) offsets[tid + 1] = incl[tid];
     if (tid == 0) offsets[0] = 0;
   }
   if (p >= P) return;
@@ -251,7 +241,7 @@ __global__ __launch_bounds__(kBP) void rank_scan_kernel(const int32_t* __restric
     for (int q = 0; q < w; ++q) r += __popc(m[q]);
     const int rank = base_s[e] + r;
     if (cap < 0 || rank < cap) {
-      row = padded ? (int)(e * cap) + rank : incl[src][e] - kept_s[e] + rank;
+      row = padded ? (int)(e * cap) + rank : incl[e] - kept_s[e] + rank;
       perm_token[row] = (int32_t)(p / k);
     }
   }

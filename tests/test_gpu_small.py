@@ -367,6 +367,52 @@ def test_padded_dispatch_matches_oracle(T, E, k, phi):
     run.free()
 
 
+@pytest.mark.parametrize("T,k,E,phi,padded", [
+    (20000, 8, 128, None, False),   # 313 dispatch blocks, dropless
+    (17000, 8, 256, 1.0, False),    # 266 blocks, capacity
+    (40000, 4, 64, 0.9, False),     # 313 blocks, capacity below the even share
+    (20000, 8, 128, 1.25, True),    # capacity-padded layout
+])
+def test_dispatch_beyond_one_rank_launch(T, k, E, phi, padded):
+    """More than 256 dispatch blocks (T k > 131072): the histogram, the scan over
+    blocks and experts, and the ranks run as three launches.  Counts, offsets,
+    row_of and the permutation bit-exact against the oracle, on random distinct
+    experts per token with a skewed expert popularity."""
+    rng = np.random.default_rng(T + E)
+    pop = rng.permutation(E)
+    keys = rng.random((T, E)) * (1.0 + pop / E)[None, :]        # some experts chosen more often
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+    assert (T * k + 511) // 512 > 256
+    cap = oracle.capacity(T, k, E, phi)
+    d = 128
+    dev_idx = torch.from_numpy(idx).cuda()
+    x = torch.zeros((T, d), dtype=torch.bfloat16, device="cuda")
+    counts = torch.full((E,), -7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -7, dtype=torch.int32, device="cuda")
+    row_of = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(_lib.moe_permute_workspace_bytes(T, k, E), 1), dtype=torch.uint8, device="cuda")
+    if padded:
+        slot = torch.full((E * cap,), -7, dtype=torch.int32, device="cuda")
+        _lib.moe_permute_padded(dev_idx, T, k, E, cap, x, d, counts, offsets, row_of, slot, None, ws)
+        torch.cuda.synchronize()
+        c_ref, o_ref, r_ref, s_ref = oracle.dispatch_padded(idx, E, cap)
+        assert np.array_equal(host(slot), s_ref)
+    else:
+        perm = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+        _lib.moe_permute(dev_idx, T, k, E, -1 if cap is None else cap, x, d, counts, offsets, row_of, perm, None, ws)
+        torch.cuda.synchronize()
+        c_ref, o_ref, r_ref, p_ref = oracle.dispatch(idx, E, cap)
+        assert np.array_equal(host(perm)[:len(p_ref)], p_ref)
+    assert np.array_equal(host(counts), c_ref)
+    assert np.array_equal(host(offsets), o_ref)
+    assert np.array_equal(host(row_of), r_ref)
+    dropped = int((r_ref < 0).sum())
+    if phi is not None and phi < 1.0:
+        assert dropped > 0
+    log(f"[dispatch T={T} k={k} E={E} phi={phi} padded={padded}] {(T * k + 511) // 512} blocks, "
+        f"{dropped} dropped: bit-exact")
+
+
 @pytest.mark.parametrize("shape", [
     S("padded_layer", "bf16", 600, 256, 8, 2, 256, 0, TK_SM, False, 1.0, False),
     S("padded_layer_shared", "bf16", 500, 256, 16, 4, 384, 256, SM_TK, True, 1.25, False),
